@@ -1,0 +1,173 @@
+"""CPU oracle for the VSA forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The GPU library never uses it.
+
+Thin ctypes binding over ``vsa_oracle.c`` (plain C, float64).  Arrays are
+numpy: bfloat16 tensors travel as ``uint16`` bit patterns, token-major
+``[S, H, 128]``.  The method follows the page "UniServe: serving FastH3 at its
+fastest" (sections "The FastH3 workload", "Fused attention preprocessing",
+"Fused output combination", "Setup"); each C function states the passage it
+implements and the reading taken where the page is open.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "vsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle_vsa.so")
+_lib = None
+
+HEAD_DIM = 128
+TILE = 64
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F64 = ctypes.c_double
+
+
+def build() -> str:
+    """Compile vsa_oracle.c (always recompiles).  No fused multiply-add
+    contraction and no fast-math: the C source's float64 operations are the
+    ones executed."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+           "-o", _LIB_PATH, _SRC, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.vsa_oracle_topk_count.argtypes = [_I64, _F64]
+        lib.vsa_oracle_topk_count.restype = _I32
+        lib.vsa_oracle_pool.argtypes = [_P, _I32, _I64, _I64, _P]
+        lib.vsa_oracle_pool.restype = None
+        lib.vsa_oracle_row_scores.argtypes = [_P, _P, _I32, _I64, _I64, _P]
+        lib.vsa_oracle_row_scores.restype = None
+        lib.vsa_oracle_select_coarse.argtypes = [_P, _P, _P, _I32, _I64, _I64, _I64, _F64,
+                                                 _P, _P, _P, _P, _P, _P, _P, ctypes.c_int]
+        lib.vsa_oracle_select_coarse.restype = _I32
+        lib.vsa_oracle_fine.argtypes = [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _I32, _P,
+                                        _P, _I64, _P, _P, ctypes.c_int]
+        lib.vsa_oracle_fine.restype = _I32
+        lib.vsa_oracle_bf16_from_f64.argtypes = [_F64]
+        lib.vsa_oracle_bf16_from_f64.restype = ctypes.c_uint16
+        lib.vsa_oracle_default_threads.argtypes = []
+        lib.vsa_oracle_default_threads.restype = _I32
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data
+
+
+def _check_tensor(x: np.ndarray, s: int, h: int) -> np.ndarray:
+    if x.dtype != np.uint16 or x.shape != (s, h, HEAD_DIM):
+        raise ValueError(f"expected uint16 [{s},{h},{HEAD_DIM}], got {x.dtype} {x.shape}")
+    return np.ascontiguousarray(x)
+
+
+def frac_as_passed(frac: float) -> float:
+    """The library takes topk_frac as a C float; the oracle widens that float."""
+    return float(np.float32(frac))
+
+
+def default_threads() -> int:
+    return int(_load().vsa_oracle_default_threads())
+
+
+def topk_count(n_v: int, frac: float) -> int:
+    return int(_load().vsa_oracle_topk_count(n_v, frac_as_passed(frac)))
+
+
+def bf16_from_f64(x: float) -> int:
+    return int(_load().vsa_oracle_bf16_from_f64(float(x)))
+
+
+def pool(x: np.ndarray, row0: int, n_tiles: int) -> np.ndarray:
+    """FP32 tile means [H][n_tiles][128] of tiles starting at token row0."""
+    x = np.ascontiguousarray(x)
+    h = x.shape[1]
+    out = np.empty((h, n_tiles, HEAD_DIM), dtype=np.float32)
+    _load().vsa_oracle_pool(_ptr(x), h, row0, n_tiles, _ptr(out))
+    return out
+
+
+def row_scores(qbar: np.ndarray, kbar: np.ndarray, h: int, u: int) -> np.ndarray:
+    n_v = qbar.shape[1]
+    s = np.empty(n_v, dtype=np.float64)
+    _load().vsa_oracle_row_scores(_ptr(np.ascontiguousarray(qbar)), _ptr(np.ascontiguousarray(kbar)),
+                                  h, n_v, u, _ptr(s))
+    return s
+
+
+def select_coarse(q, k, v, text_len, video_len, audio_len, frac, want_scores=False,
+                  threads=None) -> dict:
+    s = text_len + video_len + audio_len
+    h = q.shape[1]
+    q, k, v = (_check_tensor(x, s, h) for x in (q, k, v))
+    n_v = video_len // TILE
+    kk = topk_count(n_v, frac) if video_len % TILE == 0 else -1
+    if kk < 0:
+        raise ValueError("bad arguments")
+    qbar = np.empty((h, n_v, HEAD_DIM), np.float32)
+    kbar = np.empty_like(qbar)
+    vbar = np.empty_like(qbar)
+    sel = np.empty((h, n_v, kk), np.int32)
+    coarse = np.empty((h, n_v, HEAD_DIM), np.float64)
+    kth = np.empty((h, n_v), np.float64)
+    scores = np.empty((h, n_v, n_v), np.float64) if want_scores else None
+    r = _load().vsa_oracle_select_coarse(
+        _ptr(q), _ptr(k), _ptr(v), h, text_len, video_len, audio_len, frac_as_passed(frac),
+        _ptr(qbar), _ptr(kbar), _ptr(vbar), _ptr(sel), _ptr(coarse), _ptr(kth), _ptr(scores),
+        threads or 0)
+    if r < 0:
+        raise ValueError("bad arguments")
+    return {"k": kk, "qbar": qbar, "kbar": kbar, "vbar": vbar, "sel": sel, "coarse": coarse,
+            "kth": kth, "scores": scores}
+
+
+def fine(q, k, v, gate, text_len, video_len, audio_len, sel, coarse, rows, threads=None):
+    """Rows `rows` of every head, on the given selection.  Returns
+    (bfloat16 bits [n_rows][H][128], float64 [n_rows][H][128])."""
+    s = text_len + video_len + audio_len
+    h = q.shape[1]
+    q, k, v, gate = (_check_tensor(x, s, h) for x in (q, k, v, gate))
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    n_v = video_len // TILE
+    sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(h, n_v, -1) if n_v else \
+        np.zeros((h, 0, 0), np.int32)
+    kk = sel.shape[2] if n_v else 0
+    coarse = np.ascontiguousarray(coarse, dtype=np.float64).reshape(h, n_v, HEAD_DIM) if n_v else \
+        np.zeros((h, 0, HEAD_DIM))
+    out_b = np.empty((len(rows), h, HEAD_DIM), np.uint16)
+    out_d = np.empty((len(rows), h, HEAD_DIM), np.float64)
+    r = _load().vsa_oracle_fine(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), h, text_len, video_len,
+                                audio_len, _ptr(sel), kk, _ptr(coarse), _ptr(rows), len(rows),
+                                _ptr(out_b), _ptr(out_d), threads or 0)
+    if r < 0:
+        raise ValueError("bad arguments")
+    return out_b, out_d
+
+
+def forward(q, k, v, gate, text_len, video_len, audio_len, frac, rows=None, threads=None) -> dict:
+    """The whole path: selection, coarse, fine and combination (all rows by default)."""
+    sc = select_coarse(q, k, v, text_len, video_len, audio_len, frac, threads=threads)
+    s = text_len + video_len + audio_len
+    if rows is None:
+        rows = np.arange(s, dtype=np.int64)
+    out_b, out_d = fine(q, k, v, gate, text_len, video_len, audio_len, sc["sel"], sc["coarse"],
+                        rows, threads=threads)
+    sc.update({"rows": np.asarray(rows), "out": out_b, "out_f64": out_d})
+    return sc
