@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Benchmark of the VSA forward (one DiT attention layer) on one MI355X.
+
+One step = one full pass of the path: pooling + V packing, ranking + exact
+top-k + coarse branch, fine block-sparse attention with the gated epilogue,
+over synthetic seeded inputs already resident in HBM.  Default workload: the
+10-second shape with all 56 heads on one GPU (1,024 text + 72,576 video +
+1,024 audio tokens, 64-token tiles, k = round(0.2 * 1,134) = 227).
+
+Prints ONE JSON line.  value = effective TFLOP/s on computed tiles only
+(QK^T and PV of every computed 64x64 tile pair, 4*64*64*128 FLOP each);
+ms_per_step = ms per layer.  A 14-head run of the same shape (heads 0-13 of
+the same tensors, one SP4 rank's share) is reported under "secondary".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "VSA fwd ms/layer + effective TFLOP/s (computed tiles), 10s shape, 14 & 56 heads"
+WORKLOADS = {
+    "tiny": (1, 64, 1024, 64),
+    "5s_14h": (14, 1024, 36288, 512),
+    "10s_14h": (14, 1024, 72576, 1024),
+    "10s_56h": (56, 1024, 72576, 1024),
+}
+TILE = 64
+D = 128
+FLOP_PER_PAIR = 4 * TILE * TILE * D          # QK^T + PV of one 64x64 tile pair
+PEAK_BF16_TFLOPS = 2500.0                   # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E (published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fine_attn_traffic_10s_56h.txt")
+FINE_SOURCE = os.path.join(ROOT, "block_sparse_video_amd", "csrc", "fine_attn.hip")
+
+
+def tile_pairs(h, s_t, s_v, s_a, k):
+    n_t, n_v, n_a = s_t // TILE, s_v // TILE, s_a // TILE
+    n = n_t + n_v + n_a
+    return h * ((n_t + n_a) * n + n_v * (n_t + n_a + k))
+
+
+def pool_pack_bytes(h, s_t, s_v, s_a):
+    """Algorithmic HBM bytes of stage 1: read Q, K video rows and all V rows,
+    write pooled statistics (8 + 4 + 4 bytes per element) and the V pack."""
+    s = s_t + s_v + s_a
+    n_v = s_v // TILE
+    return 2 * s_v * h * D * 2 + s * h * D * 2 + h * n_v * D * 16 + s * h * D * 2
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic(workload):
+    """HBM bytes per launch of the fine kernel from committed rocprofv3 PMC
+    summaries, or None when absent or taken on a different kernel source."""
+    if workload != "10s_56h" or not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.lstrip().startswith("#"):
+            a, b = line.split("=", 1)
+            kv[a.strip()] = b.strip()
+    if kv.get("fine_attn_source_sha256_16") != source_hash(FINE_SOURCE):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def make_inputs(workload, threads):
+    import numpy as np
+    import synth
+    h, s_t, s_v, s_a = WORKLOADS[workload]
+    x = synth.vsa_inputs(0, h, s_t, s_v, s_a, threads=threads)
+    return {n: a for n, a in x.items()}, np
+
+
+def to_dev(a, np, torch):
+    return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def time_path(bsv, torch, xd, shape, frac, steps, warmup):
+    """Warm up, then time `steps` passes: each pass calls the three stages
+    with HIP events between them on the stream the kernels run on."""
+    h, s_t, s_v, s_a = shape
+    out, sel, ws = bsv.alloc_outputs(h, s_t, s_v, s_a, frac)
+    q, k, v, g = xd["q"], xd["k"], xd["v"], xd["gate"]
+    for _ in range(warmup):
+        bsv.vsa_forward(q, k, v, g, s_t, s_v, s_a, frac, out, sel, ws)
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        bsv.vsa_pool_pack(q, k, v, s_t, s_v, s_a, ws)
+        ev[i][1].record(stream)
+        bsv.vsa_select_coarse(h, s_t, s_v, s_a, frac, sel, ws)
+        ev[i][2].record(stream)
+        bsv.vsa_fine_attention(q, k, g, s_t, s_v, s_a, frac, sel, out, ws)
+        ev[i][3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = ev[0][0].elapsed_time(ev[-1][3]) / steps
+    stage = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps for j in range(3)]
+    # the fused entry point, same work, for reference
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        bsv.vsa_forward(q, k, v, g, s_t, s_v, s_a, frac, out, sel, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = e0.elapsed_time(e1) / steps
+    return {"ms": total_ms, "wall_ms": wall * 1e3 / steps, "stage_ms": stage, "forward_ms": fwd_ms,
+            "out": out, "sel": sel}
+
+
+def cpu_baseline(x, shape, frac, budget_rows, threads):
+    """The oracle (untuned) on a bounded sample: selection + coarse for every
+    row, the fine branch for a stratified sample of query rows."""
+    import numpy as np
+    import oracle
+    h, s_t, s_v, s_a = shape
+    n_t, n_v, n_a = s_t // TILE, s_v // TILE, s_a // TILE
+    n = n_t + n_v + n_a
+    t0 = time.perf_counter()
+    sc = oracle.select_coarse(x["q"], x["k"], x["v"], s_t, s_v, s_a, frac, threads=threads)
+    t_sel = time.perf_counter() - t0
+    kk = sc["k"]
+    stride = max(1, n_v // budget_rows)
+    rows = [s_t + u * TILE + (u % TILE) for u in range(0, n_v, stride)]
+    if s_t:
+        rows += [0, s_t - 1]
+    if s_a:
+        rows += [s_t + s_v, s_t + s_v + s_a - 1]
+    rows = np.array(sorted(set(rows)), dtype=np.int64)
+    t1 = time.perf_counter()
+    oracle.fine(x["q"], x["k"], x["v"], x["gate"], s_t, s_v, s_a, sc["sel"], sc["coarse"], rows,
+                threads=threads)
+    t_fine = time.perf_counter() - t1
+    keys = [(n if not (s_t <= r < s_t + s_v) else n_t + kk + n_a) * TILE for r in rows]
+    flops = float(sum(keys)) * h * 4 * D
+    total_flops = tile_pairs(h, s_t, s_v, s_a, kk) * FLOP_PER_PAIR
+    used = threads or oracle.default_threads()
+    return {
+        "value": flops / t_fine / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
+        "sample": (f"fine branch on {len(rows)} query rows x {h} heads (every {stride}th video tile, "
+                   f"one row each, plus first/last text and audio rows) = "
+                   f"{flops / total_flops * 100:.3f}% of the layer's computed-tile FLOPs; "
+                   f"ranking+top-k+coarse on all {h * n_v} rows took {t_sel:.2f} s"),
+        "fine_sample_s": t_fine, "select_coarse_s": t_sel,
+        "extrapolated_layer_s": t_sel + t_fine * total_flops / flops,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="10s_56h", choices=sorted(WORKLOADS))
+    ap.add_argument("--topk-frac", type=float, default=0.2)
+    ap.add_argument("--no-secondary", action="store_true", help="skip the 14-head run")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=48, help="video tiles in the oracle sample")
+    ap.add_argument("--threads", type=int, default=None, help="oracle / generator threads")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print("bench.py: this build measures one GPU only (the VSA path shards by heads with no "
+              "exchange inside it; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_video_amd as bsv
+    import synth
+
+    threads = args.threads or synth.default_threads()
+    torch.cuda.set_device(0)
+    shape = WORKLOADS[args.workload]
+    h, s_t, s_v, s_a = shape
+    frac = args.topk_frac
+    kk = bsv.vsa_topk_count(s_v, frac)
+    print(f"[bench] generating {args.workload} inputs", file=sys.stderr, flush=True)
+    x, _ = make_inputs(args.workload, threads)
+    xd = {n: to_dev(a, np, torch) for n, a in x.items()}
+    print("[bench] timing", file=sys.stderr, flush=True)
+    r = time_path(bsv, torch, xd, shape, frac, args.steps, args.warmup)
+
+    pairs = tile_pairs(h, s_t, s_v, s_a, kk)
+    flops = pairs * FLOP_PER_PAIR
+    ms = r["ms"]
+    fine_ms = r["stage_ms"][2]
+    fine_tflops = flops / (fine_ms * 1e-3) / 1e12
+    traffic = read_traffic(args.workload)
+    prop = torch.cuda.get_device_properties(0)
+    result = {
+        "metric": METRIC,
+        "value": flops / (ms * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: VSA fwd, {h} heads, d=128, text {s_t} + video "
+                               f"{s_v} + audio {s_a} tokens, 64-token tiles, k={kk}",
+                   "heads": h, "text_len": s_t, "video_len": s_v, "audio_len": s_a,
+                   "topk_frac": frac, "k": kk, "seed": 0, "inputs": "iid N(0,1) bf16",
+                   "computed_tile_pairs": pairs, "flop_per_step": flops},
+        "roofline": {"bound": "mfma", "kernel": "fine_attn", "achieved": fine_tflops,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": fine_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
+        "kernels": {
+            "pool_pack_ms": r["stage_ms"][0],
+            "pool_pack_GBs": pool_pack_bytes(h, s_t, s_v, s_a) / (r["stage_ms"][0] * 1e-3) / 1e9,
+            "select_coarse_ms": r["stage_ms"][1],
+            "fine_attn_ms": fine_ms,
+            "forward_entry_ms": r["forward_ms"],
+            "host_wall_ms_per_step": r["wall_ms"],
+        },
+        "device": {"name": prop.name, "cus": prop.multi_processor_count,
+                   "arch": getattr(prop, "gcnArchName", "")},
+    }
+    del r
+    if not args.no_secondary and h == 56:
+        x14 = {n: xd[n][:, :14].contiguous() for n in xd}
+        r14 = time_path(bsv, torch, x14, (14, s_t, s_v, s_a), frac, args.steps, args.warmup)
+        f14 = tile_pairs(14, s_t, s_v, s_a, kk) * FLOP_PER_PAIR
+        result["secondary"] = {"workload": "10s_14h (heads 0-13 of the same tensors)",
+                               "ms_per_step": r14["ms"],
+                               "value": f14 / (r14["ms"] * 1e-3) / 1e12,
+                               "fine_attn_ms": r14["stage_ms"][2],
+                               "fine_frac": f14 / (r14["stage_ms"][2] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del x14, r14
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(x, shape, frac, args.cpu_rows, threads)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+"""MI355X (gfx950) video sparse attention (VSA) forward.
+
+Python face of ``libvsa.so`` (C ABI in ``include/vsa.h``), with the same entry
+point names.  Tensors are torch tensors used as device memory only: q, k, v,
+gate and out are bfloat16 ``[S, H, 128]`` contiguous on the current GPU,
+selected_tiles is int32 ``[H, n_v, k]``, workspace is a uint8 tensor of at
+least ``vsa_workspace_bytes(...)`` bytes.  Every call enqueues on torch's
+current stream unless ``stream`` (a raw hipStream_t handle) is given.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from ._native import LIB_PATH, VsaError, load, status_string  # noqa: F401
+
+HEAD_DIM = 128
+TILE = 64
+
+__all__ = ["vsa_topk_count", "vsa_workspace_bytes", "vsa_workspace_layout", "vsa_forward",
+           "vsa_pool_pack", "vsa_select_coarse", "vsa_fine_attention", "forward", "VsaError",
+           "status_string", "LIB_PATH"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise VsaError(status, where)
+
+
+def _tensor(t, name, dtype, shape=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def vsa_topk_count(video_len: int, topk_frac: float) -> int:
+    return int(load().vsa_topk_count(video_len, topk_frac))
+
+
+def vsa_workspace_bytes(num_heads: int, text_len: int, video_len: int, audio_len: int) -> int:
+    return int(load().vsa_workspace_bytes(num_heads, text_len, video_len, audio_len))
+
+
+def vsa_workspace_layout(num_heads: int, text_len: int, video_len: int, audio_len: int) -> dict:
+    off = (ctypes.c_size_t * 6)()
+    _check(load().vsa_workspace_layout(num_heads, text_len, video_len, audio_len, off),
+           "vsa_workspace_layout")
+    names = ("qbar64", "kbar_t", "vbar", "coarse", "vpack", "total")
+    return {n: int(off[i]) for i, n in enumerate(names)}
+
+
+def _shape_args(q, text_len, video_len, audio_len):
+    s = text_len + video_len + audio_len
+    return (s, q.shape[1], HEAD_DIM)
+
+
+def vsa_forward(q, k, v, gate, text_len, video_len, audio_len, topk_frac, out, selected_tiles,
+                workspace=None, stream=None):
+    torch = _torch()
+    shp = _shape_args(q, text_len, video_len, audio_len)
+    q, k, v, out = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k"), (v, "v"),
+                                                                    (out, "out")))
+    gate = _tensor(gate, "gate", torch.bfloat16, shp)
+    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32)
+    workspace = _tensor(workspace, "workspace", torch.uint8)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(load().vsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), shp[1], text_len, video_len,
+                              audio_len, topk_frac, _ptr(out), _ptr(selected_tiles), _ptr(workspace),
+                              nbytes, _stream(stream)), "vsa_forward")
+
+
+def vsa_pool_pack(q, k, v, text_len, video_len, audio_len, workspace, stream=None):
+    torch = _torch()
+    shp = _shape_args(q, text_len, video_len, audio_len)
+    q, k, v = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k"), (v, "v")))
+    workspace = _tensor(workspace, "workspace", torch.uint8)
+    _check(load().vsa_pool_pack(_ptr(q), _ptr(k), _ptr(v), shp[1], text_len, video_len, audio_len,
+                                _ptr(workspace), workspace.numel(), _stream(stream)),
+           "vsa_pool_pack")
+
+
+def vsa_select_coarse(num_heads, text_len, video_len, audio_len, topk_frac, selected_tiles,
+                      workspace, stream=None):
+    torch = _torch()
+    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32)
+    workspace = _tensor(workspace, "workspace", torch.uint8)
+    _check(load().vsa_select_coarse(num_heads, text_len, video_len, audio_len, topk_frac,
+                                    _ptr(selected_tiles), _ptr(workspace), workspace.numel(),
+                                    _stream(stream)), "vsa_select_coarse")
+
+
+def vsa_fine_attention(q, k, gate, text_len, video_len, audio_len, topk_frac, selected_tiles, out,
+                       workspace, stream=None):
+    torch = _torch()
+    shp = _shape_args(q, text_len, video_len, audio_len)
+    q, k, out = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k"), (out, "out")))
+    gate = _tensor(gate, "gate", torch.bfloat16, shp)
+    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32)
+    workspace = _tensor(workspace, "workspace", torch.uint8)
+    _check(load().vsa_fine_attention(_ptr(q), _ptr(k), _ptr(gate), shp[1], text_len, video_len,
+                                     audio_len, topk_frac, _ptr(selected_tiles), _ptr(out),
+                                     _ptr(workspace), workspace.numel(), _stream(stream)),
+           "vsa_fine_attention")
+
+
+def alloc_outputs(num_heads, text_len, video_len, audio_len, topk_frac, device=None):
+    """Allocate (out, selected_tiles, workspace) torch tensors for one shape."""
+    torch = _torch()
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    s = text_len + video_len + audio_len
+    kk = vsa_topk_count(video_len, topk_frac)
+    if kk < 0:
+        raise ValueError("bad video_len / topk_frac")
+    n_v = video_len // TILE
+    out = torch.empty((s, num_heads, HEAD_DIM), dtype=torch.bfloat16, device=device)
+    sel = torch.empty((num_heads, n_v, kk), dtype=torch.int32, device=device)
+    wsb = vsa_workspace_bytes(num_heads, text_len, video_len, audio_len)
+    if wsb == 0:
+        raise ValueError("bad shape")
+    ws = torch.empty(wsb, dtype=torch.uint8, device=device)
+    return out, sel, ws
+
+
+def forward(q, k, v, gate, text_len, video_len, audio_len, topk_frac=0.2, workspace=None,
+            stream=None):
+    """Convenience wrapper: allocates out / selected_tiles (and the workspace
+    if none is given) with torch, then calls vsa_forward."""
+    out, sel, ws = alloc_outputs(q.shape[1], text_len, video_len, audio_len, topk_frac, q.device)
+    vsa_forward(q, k, v, gate, text_len, video_len, audio_len, topk_frac, out, sel,
+                workspace if workspace is not None else ws, stream)
+    return out, sel

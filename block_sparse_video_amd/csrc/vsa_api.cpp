@@ -1,0 +1,244 @@
+// vsa_api.cpp -- host side of the C ABI declared in include/vsa.h: argument
+// validation (before any HIP call), shape bookkeeping, workspace carving and
+// kernel launches on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "vsa.h"
+#include "vsa_internal.h"
+
+using vsa::Layout;
+using vsa::Shape;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Shape validation shared by every entry point.  No HIP call.
+vsa_status make_shape(int32_t H, int64_t S_t, int64_t S_v, int64_t S_a, Shape* s) {
+    if (H < 1 || S_t < 0 || S_v < 0 || S_a < 0) return VSA_ERR_BAD_SHAPE;
+    if (H > VSA_MAX_HEADS || S_t > VSA_MAX_TOKENS || S_v > VSA_MAX_TOKENS || S_a > VSA_MAX_TOKENS)
+        return VSA_ERR_TOO_LARGE;
+    const int64_t S = S_t + S_v + S_a;
+    if (S == 0) return VSA_ERR_BAD_SHAPE;
+    if (S_t % VSA_TILE || S_v % VSA_TILE || S_a % VSA_TILE) return VSA_ERR_UNALIGNED_LENGTH;
+    if (S > VSA_MAX_TOKENS) return VSA_ERR_TOO_LARGE;
+    if (S_v / VSA_TILE > VSA_MAX_VIDEO_TILES) return VSA_ERR_TOO_LARGE;
+    s->H = H;
+    s->S_t = S_t;
+    s->S_v = S_v;
+    s->S_a = S_a;
+    s->S = S;
+    s->n_t = (int32_t)(S_t / VSA_TILE);
+    s->n_v = (int32_t)(S_v / VSA_TILE);
+    s->n_a = (int32_t)(S_a / VSA_TILE);
+    s->N = s->n_t + s->n_v + s->n_a;
+    s->k = 0;
+    return VSA_OK;
+}
+
+int32_t topk_count(int64_t n_v, float frac) {
+    const double f = (double)frac;
+    if (!(f > 0.0 && f <= 1.0) || n_v < 0) return -1;
+    if (n_v == 0) return 0;
+    double k = std::floor(f * (double)n_v + 0.5);
+    if (k < 1.0) k = 1.0;
+    if (k > (double)n_v) k = (double)n_v;
+    return (int32_t)k;
+}
+
+vsa_status check_topk(float frac, Shape* s) {
+    const int32_t k = topk_count(s->n_v, frac);
+    if (k < 0) return VSA_ERR_BAD_TOPK;
+    s->k = k;
+    return VSA_OK;
+}
+
+vsa_status check_workspace(const void* ws, size_t bytes, const Layout& L) {
+    if (!ws) return VSA_ERR_WORKSPACE;
+    if (!aligned(ws, vsa::kAlign)) return VSA_ERR_MISALIGNED;
+    if (bytes < L.total) return VSA_ERR_WORKSPACE;
+    return VSA_OK;
+}
+
+// The kernels are written for gfx950 only.  Checked once per device.
+vsa_status check_device() {
+    static std::mutex mu;
+    static int known[64] = {0};  // 0 unknown, 1 ok, 2 wrong arch
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return VSA_ERR_HIP;
+    if (dev < 0 || dev >= 64) return VSA_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(mu);
+    if (known[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return VSA_ERR_HIP;
+        known[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    return known[dev] == 1 ? VSA_OK : VSA_ERR_DEVICE;
+}
+
+// Library-owned workspace for vsa_forward(workspace = NULL): grow-only, one per device.
+struct OwnedWorkspace {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+OwnedWorkspace g_ws[64];
+
+vsa_status owned_workspace(size_t need, void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return VSA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    OwnedWorkspace& w = g_ws[dev];
+    if (w.bytes < need) {
+        if (w.ptr) {
+            if (hipDeviceSynchronize() != hipSuccess) return VSA_ERR_HIP;
+            if (hipFree(w.ptr) != hipSuccess) return VSA_ERR_HIP;
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        if (hipMalloc(&w.ptr, need) != hipSuccess) return VSA_ERR_HIP;
+        w.bytes = need;
+    }
+    *out = w.ptr;
+    return VSA_OK;
+}
+
+vsa_status from_hip(hipError_t e) { return e == hipSuccess ? VSA_OK : VSA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* vsa_status_string(vsa_status s) {
+    switch (s) {
+        case VSA_OK: return "VSA_OK";
+        case VSA_ERR_NULL_POINTER: return "VSA_ERR_NULL_POINTER";
+        case VSA_ERR_BAD_SHAPE: return "VSA_ERR_BAD_SHAPE";
+        case VSA_ERR_UNALIGNED_LENGTH: return "VSA_ERR_UNALIGNED_LENGTH";
+        case VSA_ERR_BAD_TOPK: return "VSA_ERR_BAD_TOPK";
+        case VSA_ERR_MISALIGNED: return "VSA_ERR_MISALIGNED";
+        case VSA_ERR_WORKSPACE: return "VSA_ERR_WORKSPACE";
+        case VSA_ERR_DEVICE: return "VSA_ERR_DEVICE";
+        case VSA_ERR_HIP: return "VSA_ERR_HIP";
+        case VSA_ERR_TOO_LARGE: return "VSA_ERR_TOO_LARGE";
+    }
+    return "VSA_ERR_UNKNOWN";
+}
+
+int32_t vsa_topk_count(int64_t video_len, float topk_frac) {
+    if (video_len < 0 || video_len % VSA_TILE) return -1;
+    return topk_count(video_len / VSA_TILE, topk_frac);
+}
+
+size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_len, int64_t audio_len) {
+    Shape s;
+    if (make_shape(num_heads, text_len, video_len, audio_len, &s) != VSA_OK) return 0;
+    return vsa::make_layout(s).total;
+}
+
+vsa_status vsa_workspace_layout(int32_t num_heads, int64_t text_len, int64_t video_len,
+                                int64_t audio_len, size_t offsets[6]) {
+    if (!offsets) return VSA_ERR_NULL_POINTER;
+    Shape s;
+    vsa_status st = make_shape(num_heads, text_len, video_len, audio_len, &s);
+    if (st != VSA_OK) return st;
+    const Layout L = vsa::make_layout(s);
+    offsets[0] = L.qbar64;
+    offsets[1] = L.kbar_t;
+    offsets[2] = L.vbar;
+    offsets[3] = L.coarse;
+    offsets[4] = L.vpack;
+    offsets[5] = L.total;
+    return VSA_OK;
+}
+
+vsa_status vsa_pool_pack(const void* q, const void* k, const void* v, int32_t num_heads,
+                         int64_t text_len, int64_t video_len, int64_t audio_len, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v) return VSA_ERR_NULL_POINTER;
+    Shape s;
+    vsa_status st = make_shape(num_heads, text_len, video_len, audio_len, &s);
+    if (st != VSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16)) return VSA_ERR_MISALIGNED;
+    const Layout L = vsa::make_layout(s);
+    if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
+    if ((st = check_device()) != VSA_OK) return st;
+    return from_hip(vsa::launch_pool_pack((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                          s, (uint8_t*)workspace, L, (hipStream_t)stream));
+}
+
+vsa_status vsa_select_coarse(int32_t num_heads, int64_t text_len, int64_t video_len,
+                             int64_t audio_len, float topk_frac, int32_t* selected_tiles,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+    if (!selected_tiles) return VSA_ERR_NULL_POINTER;
+    Shape s;
+    vsa_status st = make_shape(num_heads, text_len, video_len, audio_len, &s);
+    if (st != VSA_OK) return st;
+    if (s.n_v == 0) return VSA_ERR_BAD_SHAPE;
+    if ((st = check_topk(topk_frac, &s)) != VSA_OK) return st;
+    if (!aligned(selected_tiles, 16)) return VSA_ERR_MISALIGNED;
+    const Layout L = vsa::make_layout(s);
+    if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
+    if ((st = check_device()) != VSA_OK) return st;
+    return from_hip(vsa::launch_select_coarse(s, selected_tiles, (uint8_t*)workspace, L,
+                                              (hipStream_t)stream));
+}
+
+vsa_status vsa_fine_attention(const void* q, const void* k, const void* gate, int32_t num_heads,
+                              int64_t text_len, int64_t video_len, int64_t audio_len,
+                              float topk_frac, const int32_t* selected_tiles, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !out) return VSA_ERR_NULL_POINTER;
+    if (video_len != 0 && (!gate || !selected_tiles)) return VSA_ERR_NULL_POINTER;
+    Shape s;
+    vsa_status st = make_shape(num_heads, text_len, video_len, audio_len, &s);
+    if (st != VSA_OK) return st;
+    if ((st = check_topk(topk_frac, &s)) != VSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(out, 16) || (gate && !aligned(gate, 16)) ||
+        (selected_tiles && !aligned(selected_tiles, 4)))
+        return VSA_ERR_MISALIGNED;
+    const Layout L = vsa::make_layout(s);
+    if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
+    if ((st = check_device()) != VSA_OK) return st;
+    return from_hip(vsa::launch_fine_attention((const uint16_t*)q, (const uint16_t*)k,
+                                               (const uint16_t*)gate, selected_tiles, (uint16_t*)out,
+                                               s, (const uint8_t*)workspace, L, (hipStream_t)stream));
+}
+
+vsa_status vsa_forward(const void* q, const void* k, const void* v, const void* gate,
+                       int32_t num_heads, int64_t text_len, int64_t video_len, int64_t audio_len,
+                       float topk_frac, void* out, int32_t* selected_tiles, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !out) return VSA_ERR_NULL_POINTER;
+    if (video_len != 0 && (!gate || !selected_tiles)) return VSA_ERR_NULL_POINTER;
+    Shape s;
+    vsa_status st = make_shape(num_heads, text_len, video_len, audio_len, &s);
+    if (st != VSA_OK) return st;
+    if ((st = check_topk(topk_frac, &s)) != VSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        (gate && !aligned(gate, 16)) || (selected_tiles && !aligned(selected_tiles, 16)))
+        return VSA_ERR_MISALIGNED;
+    const Layout L = vsa::make_layout(s);
+    if (workspace) {
+        if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
+    }
+    if ((st = check_device()) != VSA_OK) return st;
+    if (!workspace) {
+        if ((st = owned_workspace(L.total, &workspace)) != VSA_OK) return st;
+    }
+    hipStream_t strm = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    hipError_t e = vsa::launch_pool_pack((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                         s, ws, L, strm);
+    if (e == hipSuccess && s.n_v > 0) e = vsa::launch_select_coarse(s, selected_tiles, ws, L, strm);
+    if (e == hipSuccess)
+        e = vsa::launch_fine_attention((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)gate,
+                                       selected_tiles, (uint16_t*)out, s, ws, L, strm);
+    return from_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,56 @@
+// vsa_internal.h -- shapes, workspace layout and kernel launchers shared by
+// the host dispatcher and the gfx950 kernels of the VSA forward.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace vsa {
+
+constexpr int kD = 128;   // head dimension
+constexpr int kT = 64;    // tokens per tile
+constexpr size_t kAlign = 256;
+
+struct Shape {
+    int32_t H;
+    int64_t S_t, S_v, S_a, S;
+    int32_t n_t, n_v, n_a, N;  // tile counts
+    int32_t k;                 // selected tiles per video query tile
+};
+
+// Workspace regions (byte offsets from the workspace base).
+struct Layout {
+    size_t qbar64;  // double [H][n_v][128]
+    size_t kbar_t;  // float  [H][128][n_v]
+    size_t vbar;    // float  [H][n_v][128]
+    size_t coarse;  // float  [H][n_v][128]
+    size_t vpack;   // bf16   [H][N][128][64]  transposed, swizzled tile images
+    size_t total;
+};
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline Layout make_layout(const Shape& s) {
+    Layout L;
+    size_t off = 0;
+    const size_t hv = (size_t)s.H * (size_t)s.n_v * kD;
+    L.qbar64 = off; off = align_up(off + hv * sizeof(double));
+    L.kbar_t = off; off = align_up(off + hv * sizeof(float));
+    L.vbar = off;   off = align_up(off + hv * sizeof(float));
+    L.coarse = off; off = align_up(off + hv * sizeof(float));
+    L.vpack = off;  off = align_up(off + (size_t)s.H * (size_t)s.N * kT * kD * 2);
+    L.total = off;
+    return L;
+}
+
+// ---- launchers (each enqueues on `stream`, returns the launch status) ----
+hipError_t launch_pool_pack(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                            const Shape& s, uint8_t* ws, const Layout& L, hipStream_t stream);
+hipError_t launch_select_coarse(const Shape& s, int32_t* sel, uint8_t* ws, const Layout& L,
+                                hipStream_t stream);
+hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* k, const uint16_t* gate,
+                                 const int32_t* sel, uint16_t* out, const Shape& s,
+                                 const uint8_t* ws, const Layout& L, hipStream_t stream);
+
+}  // namespace vsa

@@ -1,0 +1,150 @@
+/*
+ * vsa.h -- C ABI of the MI355X (gfx950) video sparse attention (VSA) forward.
+ *
+ * The operation: the page "UniServe: serving FastH3 at its fastest", section
+ * "The FastH3 workload", defines VSA over a joint [text | video | audio]
+ * token sequence cut into tiles of 64 tokens, with 128-dimensional heads:
+ *   - text and audio queries attend to every key;
+ *   - a video query attends to every text and audio key and to the keys of
+ *     the video tiles its own tile selected: the top 20% (rounded to whole
+ *     tiles) by a tile score, chosen exactly (section "Setup");
+ *   - a coarse branch attends over mean-pooled tiles and is added to the
+ *     fine output through a learned gate (section "Fused output combination",
+ *     the combination equation).
+ * Section "Fused attention preprocessing" fixes the pooled statistics as
+ * FP32 and keeps top-k selection, fine attention and coarse attention as
+ * separate steps.  The algebra the page leaves open is fixed as follows:
+ *   - tile score s(u,w) = dot(pooled Q of video tile u, pooled K of video
+ *     tile w), per head, from the FP32 pooled vectors, accumulated in float64;
+ *   - k = floor(topk_frac * n_v + 0.5), clamped to [1, n_v] (0 when n_v = 0);
+ *   - ties in the ranking go to the lower tile index;
+ *   - the coarse branch: softmax over the video tiles w of s(u,w)/sqrt(128)
+ *     applied to the pooled V, one vector per video tile, added to each of
+ *     the tile's 64 rows;
+ *   - out = O_fine + sigmoid(G) * O_coarse on video rows, out = O_fine on
+ *     text and audio rows; softmax scale 1/sqrt(128); fp32 accumulation.
+ *
+ * Layout.  q, k, v, gate and out are bfloat16, token-major [S][H][128]
+ * (element (s,h,d) at index (s*H + h)*128 + d), S = text_len + video_len +
+ * audio_len, in the order text, video, audio.  Video tile u (0 <= u < n_v)
+ * is tokens text_len + 64u .. text_len + 64u + 63.  selected_tiles is int32
+ * [H][n_v][k]: for head h and video query tile u, the k selected video tiles
+ * as video-local indices (0..n_v-1), ascending.
+ *
+ * Memory and ownership.  Every tensor pointer is device memory owned by the
+ * caller, 16-byte aligned.  The library keeps no pointer after a call
+ * returns and frees nothing it was given.  The workspace is caller-owned
+ * device memory of at least vsa_workspace_bytes(...) bytes, 256-byte aligned;
+ * vsa_forward also accepts workspace == NULL, in which case it uses a
+ * grow-only buffer the library owns per device (allocated with hipMalloc on
+ * first use and on growth, after a device synchronisation; kept until the
+ * process ends).
+ *
+ * Execution.  Calls are asynchronous: on return the kernels are enqueued on
+ * `stream` (a hipStream_t, NULL = the null stream).  Argument errors are
+ * returned before any HIP call and leave every output untouched.  A launch
+ * failure returns VSA_ERR_HIP; a fault inside a kernel surfaces at the
+ * caller's next synchronisation of the stream.  Two calls that run at the
+ * same time must use different workspaces (the library-owned workspace is
+ * shared by every NULL-workspace call on a device).
+ *
+ * Limits: num_heads <= VSA_MAX_HEADS, S <= VSA_MAX_TOKENS,
+ * n_v <= VSA_MAX_VIDEO_TILES.  Head dimension is fixed at 128.
+ */
+#ifndef VSA_H
+#define VSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VSA_HEAD_DIM 128
+#define VSA_TILE 64
+#define VSA_MAX_HEADS 1024
+#define VSA_MAX_TOKENS (1LL << 24)
+#define VSA_MAX_VIDEO_TILES 16384
+
+typedef enum vsa_status {
+    VSA_OK = 0,
+    VSA_ERR_NULL_POINTER = 1,     /* a required pointer is NULL                         */
+    VSA_ERR_BAD_SHAPE = 2,        /* num_heads < 1, a negative length, or S == 0         */
+    VSA_ERR_UNALIGNED_LENGTH = 3, /* a length is not a multiple of 64                    */
+    VSA_ERR_BAD_TOPK = 4,         /* topk_frac is NaN, <= 0 or > 1                       */
+    VSA_ERR_MISALIGNED = 5,       /* a tensor is not 16-byte / workspace not 256-byte aligned */
+    VSA_ERR_WORKSPACE = 6,        /* workspace too small (or NULL where one is required) */
+    VSA_ERR_DEVICE = 7,           /* the current device is not gfx950                    */
+    VSA_ERR_HIP = 8,              /* a HIP runtime call or kernel launch failed          */
+    VSA_ERR_TOO_LARGE = 9         /* beyond VSA_MAX_HEADS / _TOKENS / _VIDEO_TILES       */
+} vsa_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* vsa_status_string(vsa_status s);
+
+/* Number of selected video tiles per video query tile (section "The FastH3
+ * workload": 20% of the video tiles, rounded to whole tiles):
+ * k = floor(topk_frac * n_v + 0.5) in double, clamped to [1, n_v];
+ * 0 when video_len == 0.  Returns -1 if video_len is negative or not a
+ * multiple of 64, or topk_frac is outside (0, 1].  Host only. */
+int32_t vsa_topk_count(int64_t video_len, float topk_frac);
+
+/* Workspace bytes needed by vsa_forward and the stage calls below for this
+ * shape; 0 if the shape is invalid.  Host only. */
+size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_len, int64_t audio_len);
+
+/* Byte offsets of the workspace regions, for inspection by tests:
+ *   offsets[0] pooled Q   float64 [H][n_v][128] (the FP32 statistic, widened)
+ *   offsets[1] pooled K   float32 [H][128][n_v] (transposed)
+ *   offsets[2] pooled V   float32 [H][n_v][128]
+ *   offsets[3] coarse     float32 [H][n_v][128]
+ *   offsets[4] packed V   bfloat16 [H][N][128][64] (per tile, transposed, swizzled)
+ *   offsets[5] total bytes (= vsa_workspace_bytes)
+ * Returns VSA_OK or a shape error.  Host only. */
+vsa_status vsa_workspace_layout(int32_t num_heads, int64_t text_len, int64_t video_len,
+                                int64_t audio_len, size_t offsets[6]);
+
+/* The whole forward pass: pooling and V packing, ranking + exact top-k +
+ * coarse branch, then fine block-sparse attention with the gated
+ * combination.  Writes out [S][H][128] bf16 and selected_tiles
+ * [H][n_v][k].  gate and selected_tiles may be NULL only when video_len is
+ * 0.  workspace may be NULL (library-owned buffer, see above). */
+vsa_status vsa_forward(const void* q, const void* k, const void* v, const void* gate,
+                       int32_t num_heads, int64_t text_len, int64_t video_len, int64_t audio_len,
+                       float topk_frac, void* out, int32_t* selected_tiles,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 1 (section "Fused attention preprocessing": FP32 tile pooling and
+ * tile packing): pooled Q, K, V of every video tile into the workspace, and
+ * V of every tile packed for the attention stage.  workspace is required. */
+vsa_status vsa_pool_pack(const void* q, const void* k, const void* v, int32_t num_heads,
+                         int64_t text_len, int64_t video_len, int64_t audio_len,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 2 (section "The FastH3 workload": ranking, exact top-k, coarse
+ * branch): reads the pooled statistics of stage 1 from the workspace,
+ * writes selected_tiles and the coarse output (workspace).  Requires
+ * video_len > 0.  workspace is required. */
+vsa_status vsa_select_coarse(int32_t num_heads, int64_t text_len, int64_t video_len,
+                             int64_t audio_len, float topk_frac, int32_t* selected_tiles,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 3 (sections "The FastH3 workload" and "Fused output combination"):
+ * fine block-sparse attention of every query tile over its key tiles, with
+ * the gated coarse term added in the epilogue.  selected_tiles may be any
+ * [H][n_v][k] array of video tile indices (k from topk_frac); indices
+ * outside [0, n_v) are clamped into it, a repeated index is attended twice,
+ * and ascending order is not required.
+ * Reads packed V and the coarse output from the workspace.  workspace is
+ * required. */
+vsa_status vsa_fine_attention(const void* q, const void* k, const void* gate, int32_t num_heads,
+                              int64_t text_len, int64_t video_len, int64_t audio_len,
+                              float topk_frac, const int32_t* selected_tiles, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VSA_H */

@@ -96,21 +96,20 @@ int32_t vsa_oracle_topk_count(int64_t n_v, double frac) {
 /* ------------------------------------------------------------------------ */
 
 /* "The FastH3 workload" (coarse branch over mean-pooled tiles) and "Fused
- * attention preprocessing" (the pooled statistics are FP32).  For each head
- * and each of n_tiles consecutive tiles starting at token row0, the mean of
- * the tile's 64 rows, summed in row order in float64 and rounded once to
- * float32.  out is [H][n_tiles][128]. */
-void vsa_oracle_pool(const uint16_t* x, int32_t H, int64_t row0, int64_t n_tiles, float* out) {
-    for (int32_t h = 0; h < H; ++h)
-        for (int64_t u = 0; u < n_tiles; ++u)
-            for (int d = 0; d < D; ++d) {
-                double s = 0.0;
-                for (int r = 0; r < T; ++r) {
-                    int64_t row = row0 + u * T + r;
-                    s += bf16_to_f64(x[(row * H + h) * D + d]);
-                }
-                out[((int64_t)h * n_tiles + u) * D + d] = (float)(s / (double)T);
-            }
+ * attention preprocessing" (the pooled statistics are FP32).  For head h and
+ * tile u (tiles counted from token row0), the mean of the tile's 64 rows,
+ * summed in row order in float64 and rounded once to float32.  out is
+ * [H][n_tiles][128]. */
+static void pool_one(const uint16_t* x, int32_t H, int64_t row0, int64_t n_tiles, int32_t h,
+                     int64_t u, float* out) {
+    for (int d = 0; d < D; ++d) {
+        double s = 0.0;
+        for (int r = 0; r < T; ++r) {
+            int64_t row = row0 + u * T + r;
+            s += bf16_to_f64(x[(row * H + h) * D + d]);
+        }
+        out[((int64_t)h * n_tiles + u) * D + d] = (float)(s / (double)T);
+    }
 }
 
 /* ------------------------------------------------------------------------ */
@@ -248,6 +247,30 @@ static void run_pool(void (*fn)(void*, int64_t, void*), void* ctx, int64_t n_ite
     free(tid);
 }
 
+typedef struct {
+    const uint16_t* x;
+    int32_t H;
+    int64_t row0, n_tiles;
+    float* out;
+} pool_ctx_t;
+
+static void pool_item(void* p, int64_t item, void* scratch) {
+    (void)scratch;
+    pool_ctx_t* c = (pool_ctx_t*)p;
+    pool_one(c->x, c->H, c->row0, c->n_tiles, (int32_t)(item / c->n_tiles), item % c->n_tiles, c->out);
+}
+
+/* Pooled FP32 means of n_tiles tiles starting at token row0, every head. */
+void vsa_oracle_pool_threads(const uint16_t* x, int32_t H, int64_t row0, int64_t n_tiles, float* out,
+                             int threads) {
+    pool_ctx_t c = {x, H, row0, n_tiles, out};
+    run_pool(pool_item, &c, (int64_t)H * n_tiles, 0, threads);
+}
+
+void vsa_oracle_pool(const uint16_t* x, int32_t H, int64_t row0, int64_t n_tiles, float* out) {
+    vsa_oracle_pool_threads(x, H, row0, n_tiles, out, 1);
+}
+
 /* ------------------------------------------------------------------------ */
 /* Steps 2-5 for every (head, video query tile)                              */
 /* ------------------------------------------------------------------------ */
@@ -293,9 +316,9 @@ int32_t vsa_oracle_select_coarse(const uint16_t* q, const uint16_t* kk, const ui
     int32_t k = vsa_oracle_topk_count(n_v, frac);
     if (k < 0) return -1;
     if (n_v == 0) return 0;
-    vsa_oracle_pool(q, H, S_t, n_v, qbar);
-    vsa_oracle_pool(kk, H, S_t, n_v, kbar);
-    vsa_oracle_pool(v, H, S_t, n_v, vbar);
+    vsa_oracle_pool_threads(q, H, S_t, n_v, qbar, threads);
+    vsa_oracle_pool_threads(kk, H, S_t, n_v, kbar, threads);
+    vsa_oracle_pool_threads(v, H, S_t, n_v, vbar, threads);
     select_ctx_t c = {qbar, kbar, vbar, n_v, k, sel, coarse, kth, scores};
     size_t scratch = sizeof(double) * (size_t)n_v + sizeof(scored_t) * (size_t)n_v;
     run_pool(select_item, &c, (int64_t)H * n_v, scratch, threads);

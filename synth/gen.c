@@ -7,11 +7,14 @@
  *
  * Definition (one normal deviate per element, independent of threading):
  *   key(seed, stream) = splitmix64(splitmix64(seed) ^ (stream * 0xD1B54A32D192ED03))
- *   for element e:  a = splitmix64(key + 2e), b = splitmix64(key + 2e + 1)
+ *   elements 2i and 2i+1 form one Box-Muller pair:
+ *                   a = splitmix64(key + 2i), b = splitmix64(key + 2i + 1)
  *                   u1 = ((a >> 11) + 1) * 2^-53        in (0, 1]
  *                   u2 =  (b >> 11)      * 2^-53        in [0, 1)
- *                   z  = sqrt(-2 ln u1) * cos(2 pi u2)  (Box-Muller, cosine branch)
- *                   value = mean + std * z, rounded to bfloat16 (nearest, ties to even)
+ *                   z[2i]   = sqrt(-2 ln u1) * cos(2 pi u2)
+ *                   z[2i+1] = sqrt(-2 ln u1) * sin(2 pi u2)
+ *                   value = mean + std * z, rounded to float32, then to
+ *                   bfloat16 (nearest, ties to even)
  * splitmix64 is the finaliser of Steele, Lea and Flood, "Fast splittable
  * pseudorandom number generators" (OOPSLA 2014).
  */
@@ -42,11 +45,25 @@ static inline uint16_t f32_to_bf16_bits(float f) {
 }
 
 static inline double normal_at(uint64_t key, uint64_t e) {
-    uint64_t a = splitmix64(key + 2 * e);
-    uint64_t b = splitmix64(key + 2 * e + 1);
+    uint64_t i = e >> 1;
+    uint64_t a = splitmix64(key + 2 * i);
+    uint64_t b = splitmix64(key + 2 * i + 1);
     double u1 = (double)((a >> 11) + 1) * 0x1p-53;
     double u2 = (double)(b >> 11) * 0x1p-53;
-    return sqrt(-2.0 * log(u1)) * cos(6.283185307179586476925286766559 * u2);
+    double r = sqrt(-2.0 * log(u1));
+    double t = 6.283185307179586476925286766559 * u2;
+    return (e & 1) ? r * sin(t) : r * cos(t);
+}
+
+static inline void normal_pair(uint64_t key, uint64_t i, double* z0, double* z1) {
+    uint64_t a = splitmix64(key + 2 * i);
+    uint64_t b = splitmix64(key + 2 * i + 1);
+    double u1 = (double)((a >> 11) + 1) * 0x1p-53;
+    double u2 = (double)(b >> 11) * 0x1p-53;
+    double r = sqrt(-2.0 * log(u1));
+    double t = 6.283185307179586476925286766559 * u2;
+    *z0 = r * cos(t);
+    *z1 = r * sin(t);
 }
 
 typedef struct {
@@ -56,13 +73,26 @@ typedef struct {
     double* out_f64;
 } job_t;
 
+static void emit(job_t* j, uint64_t i, double z) {
+    z = j->mean + j->stdv * z;
+    if (j->out_bf16) j->out_bf16[i] = f32_to_bf16_bits((float)z);
+    if (j->out_f64) j->out_f64[i] = z;
+}
+
 static void* run_job(void* p) {
     job_t* j = (job_t*)p;
-    for (uint64_t i = j->begin; i < j->end; ++i) {
-        double z = j->mean + j->stdv * normal_at(j->key, j->offset + i);
-        if (j->out_bf16) j->out_bf16[i] = f32_to_bf16_bits((float)z);
-        if (j->out_f64) j->out_f64[i] = z;
+    uint64_t i = j->begin;
+    if (i < j->end && ((j->offset + i) & 1)) {  /* odd start: second half of a pair */
+        emit(j, i, normal_at(j->key, j->offset + i));
+        ++i;
     }
+    for (; i + 1 < j->end; i += 2) {
+        double z0, z1;
+        normal_pair(j->key, (j->offset + i) >> 1, &z0, &z1);
+        emit(j, i, z0);
+        emit(j, i + 1, z1);
+    }
+    if (i < j->end) emit(j, i, normal_at(j->key, j->offset + i));
     return NULL;
 }
 

@@ -1,0 +1,112 @@
+"""Helpers of the GPU parity tests: device transfer of bfloat16 bit patterns,
+the acceptance metrics, and the selection exemption rule."""
+import numpy as np
+import torch
+
+import block_sparse_video_amd as bsv
+import oracle
+
+D = 128
+T = 64
+
+# Acceptance on bfloat16 outputs, given identical index sets.
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+# Internal gate, stricter than acceptance: relative RMS error.
+REL_RMS = 5e-3
+# Selection differences allowed only for boundary ties within this relative gap.
+TIE_REL = 1e-6
+
+
+def to_dev(bits: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to("cuda").view(torch.bfloat16)
+
+
+def from_dev_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def widen(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def inputs_to_dev(x: dict) -> dict:
+    return {n: to_dev(a) for n, a in x.items()}
+
+
+def run_forward(xd: dict, s_t, s_v, s_a, frac):
+    h = xd["q"].shape[1]
+    out, sel, ws = bsv.alloc_outputs(h, s_t, s_v, s_a, frac)
+    out.fill_(float("nan"))
+    sel.fill_(-7)
+    bsv.vsa_forward(xd["q"], xd["k"], xd["v"], xd["gate"], s_t, s_v, s_a, frac, out, sel, ws)
+    torch.cuda.synchronize()
+    return out, sel, ws
+
+
+def output_errors(got_bits: np.ndarray, ref_f64: np.ndarray) -> dict:
+    g = widen(got_bits)
+    assert np.all(np.isfinite(g)), "non-finite output"
+    err = np.abs(g - ref_f64)
+    rel = float(np.sqrt(np.sum(err ** 2)) / max(np.sqrt(np.sum(ref_f64 ** 2)), 1e-300))
+    return {"max_abs": float(err.max()), "mean_abs": float(err.mean()), "rel_rms": rel}
+
+
+def assert_outputs_close(got_bits, ref_f64, rel_rms=REL_RMS):
+    e = output_errors(got_bits, ref_f64)
+    assert e["max_abs"] <= MAX_ABS and e["mean_abs"] <= MEAN_ABS and e["rel_rms"] <= rel_rms, e
+    return e
+
+
+def check_selection(gpu_sel: np.ndarray, ref: dict, exempt_ok=True) -> int:
+    """Rows must be valid (k distinct in-range indices, ascending) and equal
+    to the oracle's, except rows whose symmetric difference consists only of
+    tiles whose oracle score lies within TIE_REL (relative) of the oracle's
+    k-th largest score.  Returns the number of exempted rows."""
+    h, n_v, kk = ref["sel"].shape
+    assert gpu_sel.shape == (h, n_v, kk)
+    assert gpu_sel.min() >= 0 and gpu_sel.max() < n_v
+    if kk > 1:
+        assert np.all(np.diff(gpu_sel, axis=-1) > 0), "rows not strictly ascending"
+    bad = np.argwhere(np.any(gpu_sel != ref["sel"], axis=-1))
+    for hh, u in bad:
+        assert exempt_ok, f"selection differs at head {hh}, tile {u}"
+        scores = oracle.row_scores(ref["qbar"], ref["kbar"], int(hh), int(u))
+        kth = ref["kth"][hh, u]
+        diff = set(gpu_sel[hh, u].tolist()) ^ set(ref["sel"][hh, u].tolist())
+        for t in diff:
+            assert abs(scores[t] - kth) <= TIE_REL * abs(kth), (hh, u, t, scores[t], kth)
+    return len(bad)
+
+
+def read_workspace(ws: torch.Tensor, h, s_t, s_v, s_a) -> dict:
+    lay = bsv.vsa_workspace_layout(h, s_t, s_v, s_a)
+    n_v = s_v // T
+    raw = ws.cpu().numpy()
+
+    def view(off, dtype, shape):
+        n = int(np.prod(shape)) * np.dtype(dtype).itemsize
+        return raw[off:off + n].view(dtype).reshape(shape)
+
+    return {"qbar64": view(lay["qbar64"], np.float64, (h, n_v, D)),
+            "kbar_t": view(lay["kbar_t"], np.float32, (h, D, n_v)),
+            "vbar": view(lay["vbar"], np.float32, (h, n_v, D)),
+            "coarse": view(lay["coarse"], np.float32, (h, n_v, D))}
+
+
+def sample_rows(s_t, s_v, s_a, n_video_tiles=6, seed=0, per_tile=(0, 21, 42, 63)):
+    """Seeded sample of query rows: first and last text and audio tiles, and
+    a few video tiles (first, last and random ones), a few rows per tile."""
+    rng = np.random.default_rng(seed)
+    tiles = []
+    n_t, n_v, n_a = s_t // T, s_v // T, s_a // T
+    if n_t:
+        tiles += [0, n_t - 1]
+    if n_v:
+        vt = {0, n_v - 1} | set(rng.choice(n_v, size=min(n_video_tiles, n_v), replace=False).tolist())
+        tiles += [n_t + u for u in sorted(vt)]
+    if n_a:
+        tiles += [n_t + n_v, n_t + n_v + n_a - 1]
+    rows = sorted({t * T + r for t in tiles for r in per_tile})
+    return np.array(rows, dtype=np.int64)

@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI (no GPU, no compute call): the library loads,
+exports every symbol include/vsa.h declares, and rejects bad arguments with
+the documented status codes before touching the GPU."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import block_sparse_video_amd as bsv
+from block_sparse_video_amd import _native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vsa.h")
+
+OK, NULLP, SHAPE, UNALIGNED, TOPK, MISALIGNED, WORKSPACE, DEVICE, HIP, TOO_LARGE = range(10)
+FAKE = 0x100000  # 256-byte aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vsa_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _native.load()
+    names = declared_functions()
+    assert {"vsa_forward", "vsa_topk_count", "vsa_workspace_bytes", "vsa_status_string",
+            "vsa_pool_pack", "vsa_select_coarse", "vsa_fine_attention",
+            "vsa_workspace_layout"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_native.SIGNATURES)
+
+
+def test_status_strings():
+    assert bsv.status_string(0) == "VSA_OK"
+    assert bsv.status_string(TOPK) == "VSA_ERR_BAD_TOPK"
+    assert bsv.status_string(99) == "VSA_ERR_UNKNOWN"
+
+
+def test_topk_count_matches_golden_table():
+    with open(os.path.join(ROOT, "tests", "golden", "topk_counts.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        assert bsv.vsa_topk_count(64 * c["n_v"], c["frac"]) == c["k"], c
+    for bad in g["invalid_fracs"]:
+        assert bsv.vsa_topk_count(640, float(bad)) == -1
+    assert bsv.vsa_topk_count(65, 0.2) == -1
+    assert bsv.vsa_topk_count(-64, 0.2) == -1
+
+
+def test_workspace_bytes_and_layout():
+    n = bsv.vsa_workspace_bytes(56, 1024, 72576, 1024)
+    lay = bsv.vsa_workspace_layout(56, 1024, 72576, 1024)
+    assert lay["total"] == n
+    h, n_v, N = 56, 1134, 1166
+    assert lay["kbar_t"] - lay["qbar64"] >= h * n_v * 128 * 8
+    assert lay["total"] - lay["vpack"] >= h * N * 64 * 128 * 2
+    assert all(v % 256 == 0 for v in lay.values())
+    assert bsv.vsa_workspace_bytes(0, 64, 64, 64) == 0
+    assert bsv.vsa_workspace_bytes(1, 63, 64, 64) == 0
+    assert bsv.vsa_workspace_bytes(1, 0, 0, 0) == 0
+    assert bsv.vsa_workspace_bytes(1, 0, 64, 0) > 0
+
+
+def fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, h=2, t=64, vid=640, au=64, frac=0.2, out=FAKE,
+             sel=FAKE, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return _native.load().vsa_forward(a["q"], a["k"], a["v"], a["g"], a["h"], a["t"], a["vid"],
+                                      a["au"], a["frac"], a["out"], a["sel"], a["ws"], a["wsb"],
+                                      a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(k=None), NULLP), (dict(v=None), NULLP), (dict(out=None), NULLP),
+    (dict(g=None), NULLP), (dict(sel=None), NULLP),
+    (dict(h=0), SHAPE), (dict(h=-3), SHAPE), (dict(t=-64), SHAPE), (dict(t=0, vid=0, au=0), SHAPE),
+    (dict(t=65), UNALIGNED), (dict(vid=100), UNALIGNED), (dict(au=1), UNALIGNED),
+    (dict(frac=0.0), TOPK), (dict(frac=-0.1), TOPK), (dict(frac=1.01), TOPK),
+    (dict(frac=float("nan")), TOPK),
+    (dict(q=FAKE + 8), MISALIGNED), (dict(out=FAKE + 2), MISALIGNED), (dict(g=FAKE + 4), MISALIGNED),
+    (dict(ws=FAKE + 16), MISALIGNED),
+    (dict(wsb=1000), WORKSPACE),
+    (dict(h=2048), TOO_LARGE), (dict(vid=64 * 20000), TOO_LARGE),
+])
+def test_forward_validation(kw, code):
+    assert fwd(**kw) == code
+
+
+def test_text_only_allows_null_gate_and_selection_up_to_validation():
+    # video_len == 0: gate/selected_tiles may be NULL; the call then fails only
+    # on the workspace size (checked before the device), never on NULL pointers.
+    assert fwd(vid=0, g=None, sel=None, wsb=10) == WORKSPACE
+
+
+def test_stage_validation():
+    lib = _native.load()
+    assert lib.vsa_pool_pack(None, FAKE, FAKE, 2, 64, 640, 64, FAKE, 1 << 40, None) == NULLP
+    assert lib.vsa_pool_pack(FAKE, FAKE, FAKE, 2, 64, 640, 64, None, 1 << 40, None) == WORKSPACE
+    assert lib.vsa_pool_pack(FAKE, FAKE, FAKE, 2, 64, 640, 64, FAKE, 64, None) == WORKSPACE
+    assert lib.vsa_select_coarse(2, 64, 640, 64, 0.2, None, FAKE, 1 << 40, None) == NULLP
+    assert lib.vsa_select_coarse(2, 64, 0, 64, 0.2, FAKE, FAKE, 1 << 40, None) == SHAPE
+    assert lib.vsa_select_coarse(2, 64, 640, 64, 2.0, FAKE, FAKE, 1 << 40, None) == TOPK
+    assert lib.vsa_fine_attention(FAKE, FAKE, FAKE, 2, 64, 640, 64, 0.2, FAKE, None, FAKE, 1 << 40,
+                                  None) == NULLP
+    assert lib.vsa_fine_attention(FAKE, FAKE, FAKE, 2, 64, 640, 64, 0.2, FAKE, FAKE, FAKE, 10,
+                                  None) == WORKSPACE
+
+
+def test_layout_rejects_bad_shape():
+    off = (ctypes.c_size_t * 6)()
+    assert _native.load().vsa_workspace_layout(1, 64, 65, 0, off) == UNALIGNED
+    assert _native.load().vsa_workspace_layout(1, 64, 64, 0, None) == NULLP

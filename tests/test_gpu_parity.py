@@ -1,0 +1,250 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Acceptance (per row): selected tiles equal the oracle's except boundary ties
+within 1e-6 relative; outputs on identical index sets within max-abs 2e-2
+and mean-abs 2e-3 of the oracle (bf16 outputs), plus a stricter internal
+relative-RMS gate of 5e-3.  Pooled statistics are compared bit for bit.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_video_amd as bsv
+import oracle
+import synth
+from tests import _gpu as G
+
+pytestmark = pytest.mark.gpu
+
+T = 64
+D = 128
+THREADS = synth.default_threads()
+BF16_NEG_INF = np.uint16(0xFF80)
+BF16_POS_INF = np.uint16(0x7F80)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    torch.cuda.set_device(0)
+    yield
+
+
+def announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def full_check(x, s_t, s_v, s_a, frac, rel_rms=G.REL_RMS, exempt_ok=True):
+    """Every row against the oracle; returns (ref, errors, gpu arrays)."""
+    xd = G.inputs_to_dev(x)
+    out, sel, ws = G.run_forward(xd, s_t, s_v, s_a, frac)
+    ref = oracle.select_coarse(x["q"], x["k"], x["v"], s_t, s_v, s_a, frac, threads=THREADS)
+    got_sel = sel.cpu().numpy()
+    if s_v:
+        G.check_selection(got_sel, ref, exempt_ok=exempt_ok)
+    rows = np.arange(s_t + s_v + s_a)
+    _, ref_out = oracle.fine(x["q"], x["k"], x["v"], x["gate"], s_t, s_v, s_a,
+                             got_sel if s_v else None, ref["coarse"], rows, threads=THREADS)
+    e = G.assert_outputs_close(G.from_dev_bits(out), ref_out, rel_rms=rel_rms)
+    return ref, e, out, got_sel, ws
+
+
+# --------------------------------------------------------------------------
+# tiny workload: 1 head, 64 text + 1024 video + 64 audio tokens, k = 3, seed 0
+# --------------------------------------------------------------------------
+
+def test_tiny_full_parity_and_stages():
+    announce("tiny 1x(64,1024,64) seed 0")
+    s_t, s_v, s_a = 64, 1024, 64
+    x = synth.vsa_inputs(0, 1, s_t, s_v, s_a)
+    ref, e, out, sel, ws = full_check(x, s_t, s_v, s_a, 0.2, exempt_ok=False)
+    assert ref["k"] == 3
+    w = G.read_workspace(ws, 1, s_t, s_v, s_a)
+    # pooled statistics: bitwise equal to the oracle's FP32 means
+    assert np.array_equal(w["qbar64"], ref["qbar"].astype(np.float64))
+    assert np.array_equal(w["kbar_t"], ref["kbar"].transpose(0, 2, 1))
+    assert np.array_equal(w["vbar"], ref["vbar"])
+    np.testing.assert_allclose(w["coarse"], ref["coarse"], rtol=2e-6, atol=1e-7)
+    print(e)
+
+
+@pytest.mark.parametrize("h,n_t,n_v,n_a,frac,seed", [
+    (2, 1, 16, 1, 0.2, 1),
+    (3, 0, 37, 0, 0.2, 2),     # video only, ragged tile count
+    (2, 2, 5, 3, 0.5, 3),
+    (1, 1, 1, 1, 0.2, 4),      # a single video tile
+    (2, 0, 2, 1, 0.2, 5),      # k clamps to 1
+    (4, 3, 70, 2, 0.3, 6),     # several select workgroups per head, ragged tail
+    (1, 2, 9, 0, 1.0, 7),      # dense (k = n_v)
+])
+def test_small_shapes_full_parity(h, n_t, n_v, n_a, frac, seed):
+    announce(f"small h={h} tiles=({n_t},{n_v},{n_a}) frac={frac} seed={seed}")
+    x = synth.vsa_inputs(seed, h, n_t * T, n_v * T, n_a * T)
+    full_check(x, n_t * T, n_v * T, n_a * T, frac, exempt_ok=False)
+
+
+def test_no_video_tiles_is_dense_attention():
+    announce("no video: h=2 tiles=(2,0,1)")
+    s_t, s_a = 128, 64
+    x = synth.vsa_inputs(8, 2, s_t, 0, s_a)
+    xd = G.inputs_to_dev(x)
+    out = torch.empty_like(xd["q"])
+    ws = torch.empty(bsv.vsa_workspace_bytes(2, s_t, 0, s_a), dtype=torch.uint8, device="cuda")
+    bsv.vsa_forward(xd["q"], xd["k"], xd["v"], None, s_t, 0, s_a, 0.2, out, None, ws)
+    torch.cuda.synchronize()
+    _, ref = oracle.fine(x["q"], x["k"], x["v"], x["gate"], s_t, 0, s_a, None, None,
+                         np.arange(s_t + s_a))
+    G.assert_outputs_close(G.from_dev_bits(out), ref)
+
+
+# --------------------------------------------------------------------------
+# structured cases
+# --------------------------------------------------------------------------
+
+def test_coarse_isolating_case():
+    """Gate at +inf (sigmoid = 1) and V carrying a per-tile offset, so the
+    coarse term is O(1): a path that dropped or misplaced the coarse branch
+    fails by far more than the tolerance."""
+    announce("coarse-isolating h=2 tiles=(1,12,1)")
+    h, s_t, s_v, s_a = 2, 64, 64 * 12, 64
+    x = synth.vsa_inputs(9, h, s_t, s_v, s_a)
+    v = G.widen(x["v"]).astype(np.float32) * 0.25
+    for u in range(12):
+        v[s_t + u * T: s_t + (u + 1) * T] += (u - 5.5) / 4
+    x["v"] = synth.f32_to_bf16_bits(v)
+    x["gate"] = np.full_like(x["gate"], BF16_POS_INF)
+    ref, e, *_ = full_check(x, s_t, s_v, s_a, 0.25, exempt_ok=False)
+    assert np.abs(ref["coarse"]).mean() > 0.1
+
+
+def test_constant_v_and_gate_extremes():
+    announce("constant V, gates -inf/0/+inf")
+    h, s_t, s_v, s_a = 3, 64, 64 * 8, 64
+    x = synth.vsa_inputs(10, h, s_t, s_v, s_a)
+    c = np.array([0.5, -1.25, 2.0], np.float32)
+    x["v"] = synth.f32_to_bf16_bits(np.broadcast_to(c[None, :, None], x["v"].shape))
+    g = np.empty_like(x["gate"])
+    g[:, 0], g[:, 1], g[:, 2] = BF16_NEG_INF, 0, BF16_POS_INF
+    x["gate"] = g
+    xd = G.inputs_to_dev(x)
+    out, sel, _ = G.run_forward(xd, s_t, s_v, s_a, 0.2)
+    o = G.widen(G.from_dev_bits(out))
+    vid = slice(s_t, s_t + s_v)
+    expect = np.broadcast_to(c[None, :, None].astype(np.float64), o.shape).copy()
+    expect[vid, 1] *= 1.5
+    expect[vid, 2] *= 2.0
+    np.testing.assert_allclose(o, expect, rtol=8e-3, atol=0)
+
+
+def test_zero_query_ties_and_duplicate_keys():
+    announce("Q = 0 and duplicated K tiles: all scores tie")
+    h, s_t, s_v, s_a = 2, 64, 64 * 20, 64
+    x = synth.vsa_inputs(11, h, s_t, s_v, s_a)
+    x0 = dict(x, q=np.zeros_like(x["q"]))
+    ref, *_ = full_check(x0, s_t, s_v, s_a, 0.2, exempt_ok=False)
+    assert np.array_equal(ref["sel"], np.broadcast_to(np.arange(4), (h, 20, 4)))
+    kdup = x["k"].copy()
+    kdup[s_t:s_t + s_v] = np.tile(x["k"][s_t:s_t + T], (20, 1, 1))
+    full_check(dict(x, k=kdup), s_t, s_v, s_a, 0.2, exempt_ok=False)
+
+
+def test_designed_ranking():
+    announce("designed ranking")
+    h, s_t, n_v = 1, 64, 15
+    s_v = n_v * T
+    x = synth.vsa_inputs(12, h, s_t, s_v, 64)
+    q = np.zeros((s_t + s_v + 64, h, D), np.float32)
+    k = np.zeros_like(q)
+    q[s_t:s_t + s_v, 0, 0] = -1.0
+    q[s_t + 7 * T: s_t + 8 * T, 0, 0] = 1.0
+    for w in range(n_v):
+        k[s_t + w * T: s_t + (w + 1) * T, 0, 0] = (w + 1) / 16
+    x["q"], x["k"] = synth.f32_to_bf16_bits(q), synth.f32_to_bf16_bits(k)
+    ref, _, _, sel, _ = full_check(x, s_t, s_v, 64, 0.2, exempt_ok=False)
+    assert np.array_equal(sel[0, 7], [12, 13, 14])
+    assert np.array_equal(sel[0, 0], [0, 1, 2])
+
+
+def test_fine_stage_on_oracle_selection():
+    """The fine stage honours the index sets it is given: run it on the
+    oracle's own selection (and on a shifted one) and compare."""
+    announce("fine stage on given selections")
+    h, s_t, s_v, s_a = 2, 64, 64 * 10, 128
+    x = synth.vsa_inputs(13, h, s_t, s_v, s_a)
+    xd = G.inputs_to_dev(x)
+    ref = oracle.select_coarse(x["q"], x["k"], x["v"], s_t, s_v, s_a, 0.3)
+    out, sel, ws = bsv.alloc_outputs(h, s_t, s_v, s_a, 0.3)
+    bsv.vsa_pool_pack(xd["q"], xd["k"], xd["v"], s_t, s_v, s_a, ws)
+    bsv.vsa_select_coarse(h, s_t, s_v, s_a, 0.3, sel, ws)
+    rows = np.arange(s_t + s_v + s_a)
+    for other in (ref["sel"], np.sort((ref["sel"] + 3) % 10, axis=-1)):
+        seld = torch.from_numpy(np.ascontiguousarray(other, dtype=np.int32)).cuda()
+        bsv.vsa_fine_attention(xd["q"], xd["k"], xd["gate"], s_t, s_v, s_a, 0.3, seld, out, ws)
+        torch.cuda.synchronize()
+        _, r = oracle.fine(x["q"], x["k"], x["v"], x["gate"], s_t, s_v, s_a, other, ref["coarse"], rows)
+        G.assert_outputs_close(G.from_dev_bits(out), r)
+
+
+def test_deterministic_and_head_slice():
+    announce("determinism + head slice")
+    s_t, s_v, s_a = 64, 64 * 24, 64
+    x4 = synth.vsa_inputs(14, 4, s_t, s_v, s_a)
+    xd4 = G.inputs_to_dev(x4)
+    o1, s1, _ = G.run_forward(xd4, s_t, s_v, s_a, 0.2)
+    o2, s2, _ = G.run_forward(xd4, s_t, s_v, s_a, 0.2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(s1, s2)
+    x2 = {n: np.ascontiguousarray(a[:, :2]) for n, a in x4.items()}
+    o3, s3, _ = G.run_forward(G.inputs_to_dev(x2), s_t, s_v, s_a, 0.2)
+    assert torch.equal(o1[:, :2].contiguous().view(torch.int16), o3.view(torch.int16))
+    assert torch.equal(s1[:2], s3)
+
+
+def test_library_owned_workspace():
+    announce("workspace = NULL")
+    s_t, s_v, s_a = 64, 64 * 8, 64
+    x = synth.vsa_inputs(15, 2, s_t, s_v, s_a)
+    xd = G.inputs_to_dev(x)
+    o1, s1, _ = G.run_forward(xd, s_t, s_v, s_a, 0.2)
+    out = torch.empty_like(o1)
+    sel = torch.empty_like(s1)
+    bsv.vsa_forward(xd["q"], xd["k"], xd["v"], xd["gate"], s_t, s_v, s_a, 0.2, out, sel, None)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), out.view(torch.int16)) and torch.equal(s1, sel)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads: every selection row, sampled output rows
+# --------------------------------------------------------------------------
+
+BIG = {
+    "5s_14h": (14, 1024, 36288, 512),
+    "10s_14h": (14, 1024, 72576, 1024),
+    "10s_56h": (56, 1024, 72576, 1024),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", list(BIG))
+def test_full_size_selection_and_sampled_rows(name):
+    h, s_t, s_v, s_a = BIG[name]
+    announce(f"full size {name}: h={h} ({s_t},{s_v},{s_a}) k={bsv.vsa_topk_count(s_v, 0.2)}")
+    x = synth.vsa_inputs(0, h, s_t, s_v, s_a, threads=THREADS)
+    xd = G.inputs_to_dev(x)
+    out, sel, ws = G.run_forward(xd, s_t, s_v, s_a, 0.2)
+    ref = oracle.select_coarse(x["q"], x["k"], x["v"], s_t, s_v, s_a, 0.2, threads=THREADS)
+    got_sel = sel.cpu().numpy()
+    n_exempt = G.check_selection(got_sel, ref)
+    w = G.read_workspace(ws, h, s_t, s_v, s_a)
+    np.testing.assert_allclose(w["coarse"], ref["coarse"], rtol=2e-5, atol=2e-7)
+    rows = G.sample_rows(s_t, s_v, s_a, n_video_tiles=3, per_tile=(0, 37, 63))
+    _, ref_out = oracle.fine(x["q"], x["k"], x["v"], x["gate"], s_t, s_v, s_a, got_sel,
+                             ref["coarse"], rows, threads=THREADS)
+    got = G.from_dev_bits(out)[rows]
+    e = G.assert_outputs_close(got, ref_out)
+    assert np.isfinite(G.widen(G.from_dev_bits(out[::997]))).all()
+    print(name, "exempt rows:", n_exempt, e, flush=True)
+    del xd, out, ws
+    torch.cuda.empty_cache()
