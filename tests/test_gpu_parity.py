@@ -113,7 +113,7 @@ def test_coarse_isolating_case():
     x = synth.vsa_inputs(9, h, s_t, s_v, s_a)
     v = G.widen(x["v"]).astype(np.float32) * 0.25
     for u in range(12):
-        v[s_t + u * T: s_t + (u + 1) * T] += (u - 5.5) / 4
+        v[s_t + u * T: s_t + (u + 1) * T] += (u + 1) / 8  # same sign: survives the coarse average
     x["v"] = synth.f32_to_bf16_bits(v)
     x["gate"] = np.full_like(x["gate"], BF16_POS_INF)
     ref, e, *_ = full_check(x, s_t, s_v, s_a, 0.25, exempt_ok=False)
