@@ -20,11 +20,6 @@ namespace {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Swizzle of the packed V tile: 8-byte chunk c (keys 4c..4c+3) of row d is
-// stored at chunk position c ^ vswz(d).  With it, 32 consecutive rows read at
-// the same logical chunk hit distinct LDS banks (see fine_attn.hip).
-__device__ __forceinline__ int vswz(int d) { return (d & 15) ^ ((d >> 4) & 1); }
-
 // grid (n_v, ceil(H/8), 2): z = 0 pools Q, z = 1 pools K.  128 threads = 8
 // heads x 16 column chunks of 8 dims; each thread walks the tile's 64 rows.
 __global__ __launch_bounds__(128) void pool_qk_kernel(const uint16_t* __restrict__ q,
@@ -66,9 +61,9 @@ __global__ __launch_bounds__(128) void pool_qk_kernel(const uint16_t* __restrict
 }
 
 // grid (N, H), 256 threads.  Loads one 64 x 128 V tile of one head into LDS,
-// writes its pooled mean (video tiles) and its transposed, swizzled image
-// [128 d][64 keys] (16 KiB, the exact byte image the attention stage copies
-// into LDS).
+// writes its pooled mean (video tiles) and its transpose, split by key
+// halves: [2 halves][128 d][32 keys] bf16 (16 KiB), so that each half-tile
+// of V^T is one contiguous 8 KiB block for the attention stage.
 constexpr int kPitch = kD + 8;  // LDS row pitch in bf16 elements (272 bytes)
 
 __global__ __launch_bounds__(256) void pack_v_kernel(const uint16_t* __restrict__ v, int H,
@@ -98,20 +93,16 @@ __global__ __launch_bounds__(256) void pack_v_kernel(const uint16_t* __restrict_
     uint16_t* dst = vpack + ((int64_t)h * N + t) * (kT * kD);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        // 16-byte piece id: half (1 bit) | d (7 bits) | piece of 8 keys (2 bits)
         const int id = tid + 256 * i;
-        const int d = id >> 3, jpair = id & 7;
+        const int half = id >> 9, d = (id >> 2) & 127, piece = id & 3;
+        const int key0 = 32 * half + 8 * piece;
         uint32_t wds[4];
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int c = (2 * jpair + half) ^ vswz(d);
-            const uint32_t e0 = tile[(4 * c + 0) * kPitch + d];
-            const uint32_t e1 = tile[(4 * c + 1) * kPitch + d];
-            const uint32_t e2 = tile[(4 * c + 2) * kPitch + d];
-            const uint32_t e3 = tile[(4 * c + 3) * kPitch + d];
-            wds[2 * half + 0] = e0 | (e1 << 16);
-            wds[2 * half + 1] = e2 | (e3 << 16);
-        }
-        *(uint4*)(dst + d * kT + 8 * jpair) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
+        for (int e = 0; e < 4; ++e)
+            wds[e] = (uint32_t)tile[(key0 + 2 * e) * kPitch + d] |
+                     ((uint32_t)tile[(key0 + 2 * e + 1) * kPitch + d] << 16);
+        *(uint4*)(dst + id * 8) = make_uint4(wds[0], wds[1], wds[2], wds[3]);
     }
 }
 
