@@ -108,7 +108,7 @@ def time_path(bsv, torch, xd, shape, frac, steps, warmup):
         ev[i][1].record(stream)
         bsv.vsa_select_coarse(h, s_t, s_v, s_a, frac, sel, ws)
         ev[i][2].record(stream)
-        bsv.vsa_fine_attention(q, k, g, s_t, s_v, s_a, frac, sel, out, ws)
+        bsv.vsa_fine_attention(q, g, s_t, s_v, s_a, frac, sel, out, ws)
         ev[i][3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

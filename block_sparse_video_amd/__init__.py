@@ -65,10 +65,10 @@ def vsa_workspace_bytes(num_heads: int, text_len: int, video_len: int, audio_len
 
 
 def vsa_workspace_layout(num_heads: int, text_len: int, video_len: int, audio_len: int) -> dict:
-    off = (ctypes.c_size_t * 6)()
+    off = (ctypes.c_size_t * 7)()
     _check(load().vsa_workspace_layout(num_heads, text_len, video_len, audio_len, off),
            "vsa_workspace_layout")
-    names = ("qbar64", "kbar_t", "vbar", "coarse", "vpack", "total")
+    names = ("qbar64", "kbar_t", "vbar", "coarse", "kpack", "vpack", "total")
     return {n: int(off[i]) for i, n in enumerate(names)}
 
 
@@ -112,15 +112,15 @@ def vsa_select_coarse(num_heads, text_len, video_len, audio_len, topk_frac, sele
                                     _stream(stream)), "vsa_select_coarse")
 
 
-def vsa_fine_attention(q, k, gate, text_len, video_len, audio_len, topk_frac, selected_tiles, out,
+def vsa_fine_attention(q, gate, text_len, video_len, audio_len, topk_frac, selected_tiles, out,
                        workspace, stream=None):
     torch = _torch()
     shp = _shape_args(q, text_len, video_len, audio_len)
-    q, k, out = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k"), (out, "out")))
+    q, out = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (out, "out")))
     gate = _tensor(gate, "gate", torch.bfloat16, shp)
     selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32)
     workspace = _tensor(workspace, "workspace", torch.uint8)
-    _check(load().vsa_fine_attention(_ptr(q), _ptr(k), _ptr(gate), shp[1], text_len, video_len,
+    _check(load().vsa_fine_attention(_ptr(q), _ptr(gate), shp[1], text_len, video_len,
                                      audio_len, topk_frac, _ptr(selected_tiles), _ptr(out),
                                      _ptr(workspace), workspace.numel(), _stream(stream)),
            "vsa_fine_attention")

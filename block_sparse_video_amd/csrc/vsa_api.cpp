@@ -141,7 +141,7 @@ size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_le
 }
 
 vsa_status vsa_workspace_layout(int32_t num_heads, int64_t text_len, int64_t video_len,
-                                int64_t audio_len, size_t offsets[6]) {
+                                int64_t audio_len, size_t offsets[7]) {
     if (!offsets) return VSA_ERR_NULL_POINTER;
     Shape s;
     vsa_status st = make_shape(num_heads, text_len, video_len, audio_len, &s);
@@ -151,8 +151,9 @@ vsa_status vsa_workspace_layout(int32_t num_heads, int64_t text_len, int64_t vid
     offsets[1] = L.kbar_t;
     offsets[2] = L.vbar;
     offsets[3] = L.coarse;
-    offsets[4] = L.vpack;
-    offsets[5] = L.total;
+    offsets[4] = L.kpack;
+    offsets[5] = L.vpack;
+    offsets[6] = L.total;
     return VSA_OK;
 }
 
@@ -188,24 +189,23 @@ vsa_status vsa_select_coarse(int32_t num_heads, int64_t text_len, int64_t video_
                                               (hipStream_t)stream));
 }
 
-vsa_status vsa_fine_attention(const void* q, const void* k, const void* gate, int32_t num_heads,
+vsa_status vsa_fine_attention(const void* q, const void* gate, int32_t num_heads,
                               int64_t text_len, int64_t video_len, int64_t audio_len,
                               float topk_frac, const int32_t* selected_tiles, void* out,
                               void* workspace, size_t workspace_bytes, void* stream) {
-    if (!q || !k || !out) return VSA_ERR_NULL_POINTER;
+    if (!q || !out) return VSA_ERR_NULL_POINTER;
     if (video_len != 0 && (!gate || !selected_tiles)) return VSA_ERR_NULL_POINTER;
     Shape s;
     vsa_status st = make_shape(num_heads, text_len, video_len, audio_len, &s);
     if (st != VSA_OK) return st;
     if ((st = check_topk(topk_frac, &s)) != VSA_OK) return st;
-    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(out, 16) || (gate && !aligned(gate, 16)) ||
+    if (!aligned(q, 16) || !aligned(out, 16) || (gate && !aligned(gate, 16)) ||
         (selected_tiles && !aligned(selected_tiles, 4)))
         return VSA_ERR_MISALIGNED;
     const Layout L = vsa::make_layout(s);
     if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
     if ((st = check_device()) != VSA_OK) return st;
-    return from_hip(vsa::launch_fine_attention((const uint16_t*)q, (const uint16_t*)k,
-                                               (const uint16_t*)gate, selected_tiles, (uint16_t*)out,
+    return from_hip(vsa::launch_fine_attention((const uint16_t*)q, (const uint16_t*)gate, selected_tiles, (uint16_t*)out,
                                                s, (const uint8_t*)workspace, L, (hipStream_t)stream));
 }
 
@@ -236,7 +236,7 @@ vsa_status vsa_forward(const void* q, const void* k, const void* v, const void* 
                                          s, ws, L, strm);
     if (e == hipSuccess && s.n_v > 0) e = vsa::launch_select_coarse(s, selected_tiles, ws, L, strm);
     if (e == hipSuccess)
-        e = vsa::launch_fine_attention((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)gate,
+        e = vsa::launch_fine_attention((const uint16_t*)q, (const uint16_t*)gate,
                                        selected_tiles, (uint16_t*)out, s, ws, L, strm);
     return from_hip(e);
 }

@@ -25,7 +25,8 @@ struct Layout {
     size_t kbar_t;  // float  [H][128][n_v]
     size_t vbar;    // float  [H][n_v][128]
     size_t coarse;  // float  [H][n_v][128]
-    size_t vpack;   // bf16   [H][N][128][64]  transposed, swizzled tile images
+    size_t kpack;   // bf16   [H][N][2][8][64][8]      K tiles in MFMA A-operand order
+    size_t vpack;   // bf16   [H][N][2][4][2][64][8]   V^T tiles in MFMA A-operand order
     size_t total;
 };
 
@@ -39,6 +40,7 @@ inline Layout make_layout(const Shape& s) {
     L.kbar_t = off; off = align_up(off + hv * sizeof(float));
     L.vbar = off;   off = align_up(off + hv * sizeof(float));
     L.coarse = off; off = align_up(off + hv * sizeof(float));
+    L.kpack = off;  off = align_up(off + (size_t)s.H * (size_t)s.N * kT * kD * 2);
     L.vpack = off;  off = align_up(off + (size_t)s.H * (size_t)s.N * kT * kD * 2);
     L.total = off;
     return L;
@@ -49,7 +51,7 @@ hipError_t launch_pool_pack(const uint16_t* q, const uint16_t* k, const uint16_t
                             const Shape& s, uint8_t* ws, const Layout& L, hipStream_t stream);
 hipError_t launch_select_coarse(const Shape& s, int32_t* sel, uint8_t* ws, const Layout& L,
                                 hipStream_t stream);
-hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* k, const uint16_t* gate,
+hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate,
                                  const int32_t* sel, uint16_t* out, const Shape& s,
                                  const uint8_t* ws, const Layout& L, hipStream_t stream);
 

@@ -99,11 +99,12 @@ size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_le
  *   offsets[1] pooled K   float32 [H][128][n_v] (transposed)
  *   offsets[2] pooled V   float32 [H][n_v][128]
  *   offsets[3] coarse     float32 [H][n_v][128]
- *   offsets[4] packed V   bfloat16 [H][N][128][64] (per tile, transposed, swizzled)
- *   offsets[5] total bytes (= vsa_workspace_bytes)
+ *   offsets[4] packed K   bfloat16, 16 KiB per (head, tile), in MFMA operand order
+ *   offsets[5] packed V   bfloat16, 16 KiB per (head, tile), in MFMA operand order
+ *   offsets[6] total bytes (= vsa_workspace_bytes)
  * Returns VSA_OK or a shape error.  Host only. */
 vsa_status vsa_workspace_layout(int32_t num_heads, int64_t text_len, int64_t video_len,
-                                int64_t audio_len, size_t offsets[6]);
+                                int64_t audio_len, size_t offsets[7]);
 
 /* The whole forward pass: pooling and V packing, ranking + exact top-k +
  * coarse branch, then fine block-sparse attention with the gated
@@ -117,7 +118,8 @@ vsa_status vsa_forward(const void* q, const void* k, const void* v, const void* 
 
 /* Stage 1 (section "Fused attention preprocessing": FP32 tile pooling and
  * tile packing): pooled Q, K, V of every video tile into the workspace, and
- * V of every tile packed for the attention stage.  workspace is required. */
+ * K and V of every tile packed for the attention stage.  workspace is
+ * required. */
 vsa_status vsa_pool_pack(const void* q, const void* k, const void* v, int32_t num_heads,
                          int64_t text_len, int64_t video_len, int64_t audio_len,
                          void* workspace, size_t workspace_bytes, void* stream);
@@ -136,9 +138,9 @@ vsa_status vsa_select_coarse(int32_t num_heads, int64_t text_len, int64_t video_
  * [H][n_v][k] array of video tile indices (k from topk_frac); indices
  * outside [0, n_v) are clamped into it, a repeated index is attended twice,
  * and ascending order is not required.
- * Reads packed V and the coarse output from the workspace.  workspace is
- * required. */
-vsa_status vsa_fine_attention(const void* q, const void* k, const void* gate, int32_t num_heads,
+ * Reads the packed K and V tiles and the coarse output that stages 1 and 2
+ * left in the workspace.  workspace is required. */
+vsa_status vsa_fine_attention(const void* q, const void* gate, int32_t num_heads,
                               int64_t text_len, int64_t video_len, int64_t audio_len,
                               float topk_frac, const int32_t* selected_tiles, void* out,
                               void* workspace, size_t workspace_bytes, void* stream);

@@ -59,6 +59,7 @@ def test_workspace_bytes_and_layout():
     h, n_v, N = 56, 1134, 1166
     assert lay["kbar_t"] - lay["qbar64"] >= h * n_v * 128 * 8
     assert lay["total"] - lay["vpack"] >= h * N * 64 * 128 * 2
+    assert lay["vpack"] - lay["kpack"] >= h * N * 64 * 128 * 2
     assert all(v % 256 == 0 for v in lay.values())
     assert bsv.vsa_workspace_bytes(0, 64, 64, 64) == 0
     assert bsv.vsa_workspace_bytes(1, 63, 64, 64) == 0
@@ -105,13 +106,13 @@ def test_stage_validation():
     assert lib.vsa_select_coarse(2, 64, 640, 64, 0.2, None, FAKE, 1 << 40, None) == NULLP
     assert lib.vsa_select_coarse(2, 64, 0, 64, 0.2, FAKE, FAKE, 1 << 40, None) == SHAPE
     assert lib.vsa_select_coarse(2, 64, 640, 64, 2.0, FAKE, FAKE, 1 << 40, None) == TOPK
-    assert lib.vsa_fine_attention(FAKE, FAKE, FAKE, 2, 64, 640, 64, 0.2, FAKE, None, FAKE, 1 << 40,
+    assert lib.vsa_fine_attention(FAKE, FAKE, 2, 64, 640, 64, 0.2, FAKE, None, FAKE, 1 << 40,
                                   None) == NULLP
-    assert lib.vsa_fine_attention(FAKE, FAKE, FAKE, 2, 64, 640, 64, 0.2, FAKE, FAKE, FAKE, 10,
+    assert lib.vsa_fine_attention(FAKE, FAKE, 2, 64, 640, 64, 0.2, FAKE, FAKE, FAKE, 10,
                                   None) == WORKSPACE
 
 
 def test_layout_rejects_bad_shape():
-    off = (ctypes.c_size_t * 6)()
+    off = (ctypes.c_size_t * 7)()
     assert _native.load().vsa_workspace_layout(1, 64, 65, 0, off) == UNALIGNED
     assert _native.load().vsa_workspace_layout(1, 64, 64, 0, None) == NULLP

@@ -182,7 +182,7 @@ def test_fine_stage_on_oracle_selection():
     rows = np.arange(s_t + s_v + s_a)
     for other in (ref["sel"], np.sort((ref["sel"] + 3) % 10, axis=-1)):
         seld = torch.from_numpy(np.ascontiguousarray(other, dtype=np.int32)).cuda()
-        bsv.vsa_fine_attention(xd["q"], xd["k"], xd["gate"], s_t, s_v, s_a, 0.3, seld, out, ws)
+        bsv.vsa_fine_attention(xd["q"], xd["gate"], s_t, s_v, s_a, 0.3, seld, out, ws)
         torch.cuda.synchronize()
         _, r = oracle.fine(x["q"], x["k"], x["v"], x["gate"], s_t, s_v, s_a, other, ref["coarse"], rows)
         G.assert_outputs_close(G.from_dev_bits(out), r)
