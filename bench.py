@@ -175,6 +175,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=48, help="video tiles in the oracle sample")
     ap.add_argument("--threads", type=int, default=None, help="oracle / generator threads")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before timing, run one plain device copy of this many MiB (a known-size "
+                         "reference for HBM byte counters under rocprofv3 --pmc)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -198,6 +201,16 @@ def main():
     print(f"[bench] generating {args.workload} inputs", file=sys.stderr, flush=True)
     x, _ = make_inputs(args.workload, threads)
     xd = {n: to_dev(a, np, torch) for n, a in x.items()}
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy: {n} bytes read, {n} bytes written", file=sys.stderr,
+              flush=True)
+        del src, dst
     print("[bench] timing", file=sys.stderr, flush=True)
     r = time_path(bsv, torch, xd, shape, frac, args.steps, args.warmup)
 
