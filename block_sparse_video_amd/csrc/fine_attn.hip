@@ -12,10 +12,11 @@
 // One wavefront computes one work unit (head h, query tile j): 64 query rows
 // against every key tile of the unit's list, walked as half-tiles of 32 keys.
 // Every K/V element a unit needs is used by that wavefront only, so the
-// wavefront streams its operands into a private 32 KiB LDS ring (two K slots,
-// two V slots) with global_load_lds_dwordx4 and needs no barriers.  Stage 1
-// stored the K and V tiles in the exact per-lane operand order, so every load
-// and every LDS operand read is one contiguous 1 KiB wavefront access.
+// wavefront streams its operands into a private 40 KiB LDS ring (three K
+// slots, two V slots) with global_load_lds_dwordx4 and needs no barriers.
+// Stage 1 stored the K and V tiles in the exact per-lane operand order, so
+// every load and every LDS operand read is one contiguous 1 KiB wavefront
+// access.
 //
 // Per half-tile, for each of the two 32-query blocks qb:
 //   S^T[qb] (32 keys x 32 queries) = K Q^T  -- eight v_mfma_f32_32x32x16_bf16
@@ -23,10 +24,9 @@
 //   (each lane owns one column and 16 of its 32 scores; lane ^ 32 owns the
 //   other 16)
 //   O^T[qb] (128 dims x 32 queries) += V^T P^T  -- eight more MFMAs
-// Software pipeline: the S^T MFMAs of the next half-tile are issued in the
-// same step as the softmax numerators of the current one, so matrix and
-// vector units overlap within the wavefront; K is fetched two half-tiles
-// ahead of its use, V one.
+// Software pipeline: step x issues the S^T MFMAs of half-tile x+1 and the PV
+// MFMAs of half-tile x-1 while the vector unit computes the numerators of
+// half-tile x, so no MFMA of a step depends on that step's vector work.
 //
 // Accumulator layout of a 32x32 MFMA (lane l, element i of the 16 floats):
 //   row = 8*(i/4) + 4*(l/32) + (i%4), column = l%32.
@@ -59,51 +59,26 @@ struct FineArgs {
     float scale_log2;  // log2(e) / sqrt(128)
 };
 
-// blockIdx -> (head, query tile).  Workgroups are dealt round-robin to the 8
-// XCDs, so XCD x runs blocks x, x+8, x+16, ...  Each XCD is given one
-// contiguous range of the head-major unit order (a few heads, so its L2 sees
-// one head's K/V at a time), and inside its range the dense text/audio
-// units (N key tiles each) are issued before the video units (n_t+k+n_a).
-__device__ __forceinline__ void unit_of(int b, int H, int N, int n_t, int n_v, int n_a, int& h,
-                                        int& j) {
+// blockIdx -> (head, query tile).  All video units come first, head-major,
+// then all dense text/audio units.  Workgroups are dealt round-robin to the 8
+// XCDs, so during the video phase every XCD works on the same one or two
+// heads: the K/V tiles in flight (37 MB per head at the 10 s shape) stay
+// within the last-level cache, and the ~1,000 concurrently resident units
+// of one head start together and sweep their ascending key lists at the same
+// pace.  The dense units (N key tiles each, ~4.5x a video unit) then start
+// together and sweep every tile of their heads in step.
+__device__ __forceinline__ void unit_of(int b, int H, int n_t, int n_v, int n_a, int& h, int& j) {
     const int n_h = n_t + n_a;
-    const int64_t G = (int64_t)H * N;
-    const int x = b & 7;
-    const int64_t i = b >> 3;
-    const int64_t G8 = G >> 3, rem = G & 7;
-    const int64_t a = (int64_t)x * G8 + (x < rem ? x : rem);
-    const int64_t cnt = G8 + (x < rem ? 1 : 0);
-    const int hA = (int)(a / N), hB = (int)((a + cnt - 1) / N);
-    int64_t heavy_total = 0;
-    for (int hh = hA; hh <= hB; ++hh) {
-        const int64_t base = (int64_t)hh * N;
-        const int64_t lo = a > base ? a : base;
-        const int64_t hi0 = a + cnt, hi1 = base + n_h;
-        const int64_t hi = hi0 < hi1 ? hi0 : hi1;
-        if (hi > lo) heavy_total += hi - lo;
+    const int V = H * n_v;
+    if (b < V) {
+        h = b / n_v;
+        j = n_t + (b - h * n_v);
+    } else {
+        const int c = b - V;
+        h = c / n_h;
+        const int p = c - h * n_h;
+        j = p < n_t ? p : n_v + p;
     }
-    const bool want_heavy = i < heavy_total;
-    int64_t rank = want_heavy ? i : i - heavy_total;
-    int64_t pos = a;
-    for (int hh = hA; hh <= hB; ++hh) {
-        const int64_t base = (int64_t)hh * N;
-        const int64_t lo_all = a > base ? a : base;
-        const int64_t hi_all = (a + cnt) < (base + N) ? (a + cnt) : (base + N);
-        const int64_t hv_lo = lo_all, hv_hi = hi_all < base + n_h ? hi_all : base + n_h;
-        const int64_t nh = hv_hi > hv_lo ? hv_hi - hv_lo : 0;
-        const int64_t vd_lo = lo_all > base + n_h ? lo_all : base + n_h;
-        const int64_t nv = hi_all > vd_lo ? hi_all - vd_lo : 0;
-        if (want_heavy) {
-            if (rank < nh) { pos = hv_lo + rank; break; }
-            rank -= nh;
-        } else {
-            if (rank < nv) { pos = vd_lo + rank; break; }
-            rank -= nv;
-        }
-    }
-    h = (int)(pos / N);
-    const int p = (int)(pos - (int64_t)h * N);
-    j = p < n_h ? (p < n_t ? p : n_v + p) : n_t + (p - n_h);
 }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -136,14 +111,29 @@ __device__ __forceinline__ int load_uniform(const int32_t* p) {
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// Start the copy of one packed half-tile operand block (8 KiB, 8 x 1 KiB) from
-// global memory into an LDS slot: `src` is the block's (wave-uniform) byte
-// address, `lane_off` = 16 * lane.  Completion is tracked by vmcnt only.
-__device__ __forceinline__ void fetch_half(unsigned char* slot, const char* src, uint32_t lane_off) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(src + (lane_off + i * 1024u)),
-                                         (lds_ptr_t)(slot + i * 1024), 16, 0, 0);
+// Start the copy of one packed half-tile operand block (8 KiB = 8 x 1 KiB)
+// from global memory straight into an LDS slot: eight global_load_lds_dwordx4
+// with a wave-uniform 64-bit base in SGPRs and the per-lane offsets
+// voff[i] = 16 * lane + 1024 * i, so issuing them costs no vector ALU work.
+// M0 holds the LDS destination of each 1 KiB piece (lane l writes bytes
+// 16l .. 16l+15 of it).  Nothing else in the kernel uses M0.  Completion is
+// tracked by vmcnt only; the compiler does not see these loads, so every
+// consumer waits with an explicit vmcnt value.
+__device__ __forceinline__ void fetch_half(uint32_t slot, const char* base, const uint32_t (&voff)[8]) {
+    asm volatile(
+        "s_mov_b32 m0, %[s]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v0], %[b]\n\t"
+        "s_add_u32 m0, %[s], 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v1], %[b]\n\t"
+        "s_add_u32 m0, %[s], 0x800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v2], %[b]\n\t"
+        "s_add_u32 m0, %[s], 0xc00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v3], %[b]\n\t"
+        "s_add_u32 m0, %[s], 0x1000\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v4], %[b]\n\t"
+        "s_add_u32 m0, %[s], 0x1400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v5], %[b]\n\t"
+        "s_add_u32 m0, %[s], 0x1800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v6], %[b]\n\t"
+        "s_add_u32 m0, %[s], 0x1c00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v7], %[b]"
+        :
+        : [s] "s"(slot), [b] "s"(base), [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]),
+          [v3] "v"(voff[3]), [v4] "v"(voff[4]), [v5] "v"(voff[5]), [v6] "v"(voff[6]),
+          [v7] "v"(voff[7])
+        : "memory", "m0", "scc");
 }
 
 // Wait until at most n of this wave's vector-memory loads are outstanding
@@ -151,21 +141,17 @@ __device__ __forceinline__ void fetch_half(unsigned char* slot, const char* src,
 // their "no wait" maxima).  The compiler does not track the LDS writes of
 // global_load_lds, so these waits are what makes a ring slot readable.
 __device__ __forceinline__ void wait_vmcnt(int n) {
-    if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);       // vmcnt(16)
+    if (n >= 32) __builtin_amdgcn_s_waitcnt(0x8F70);       // vmcnt(32)
+    else if (n >= 24) __builtin_amdgcn_s_waitcnt(0x4F78);  // vmcnt(24)
+    else if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);  // vmcnt(16)
     else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
     else __builtin_amdgcn_s_waitcnt(0x0F70);               // vmcnt(0)
     asm volatile("" ::: "memory");
 }
 
-// S^T (32 keys x 32 queries) of one query block: eight MFMAs over the 128
-// dims, K operands read from an LDS slot (lane-contiguous, conflict-free).
-__device__ __forceinline__ f32x16 qk_block(const bf16x8* kslot, const bf16x8 (&q)[8]) {
-    f32x16 acc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc = mfma32(kslot[s * 64], q[s], acc);
-    return acc;
+// Wait for every outstanding LDS read (and scalar load) of this wave.
+__device__ __forceinline__ void wait_lgkm() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
 // Reference-scaled softmax numerators of one 32-query block over one
@@ -199,39 +185,38 @@ __device__ __forceinline__ float column_max(const f32x16& s, float c2) {
     return xhalf_max(mx) * c2;
 }
 
-// O^T[qb] += V^T P^T for both query blocks; each V operand is read from the
-// LDS slot once and used by both blocks.
-__device__ __forceinline__ void pv(f32x16 (&o)[2][4], const bf16x8* vslot, const bf16x8 (&p)[2][2]) {
+// The four packed operand blocks (8 K or V operands of one half-tile) this
+// lane reads from a ring slot: operand i is at byte 1024 i + 16 lane.
+typedef __attribute__((address_space(3))) const bf16x8* lds_bf16x8_ptr;
+__device__ __forceinline__ void read_ops(bf16x8 (&op)[8], uint32_t slot, int lane) {
+    const lds_bf16x8_ptr p = (lds_bf16x8_ptr)(uintptr_t)slot + lane;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const bf16x8 v = vslot[(2 * db + m) * 64];
-#pragma unroll
-            for (int qb = 0; qb < 2; ++qb) o[qb][db] = mfma32(v, p[qb][m], o[qb][db]);
-        }
+    for (int i = 0; i < 8; ++i) op[i] = p[i * 64];
 }
 
 __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
-    // Ring: K slots at 0 and 8 KiB, V slots at 16 and 24 KiB.  After the loop
-    // the same 32 KiB stage the fp32 output.
-    __shared__ __align__(1024) unsigned char lds[4 * 8192];
-    unsigned char* const kslot[2] = {lds, lds + 8192};
-    unsigned char* const vslot[2] = {lds + 16384, lds + 24576};
+    // Ring: K slots at 0, 8 and 16 KiB, V slots at 24 and 32 KiB.  After the
+    // loop the first 32 KiB stage the fp32 output.
+    __shared__ __align__(1024) unsigned char lds[5 * 8192];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+    const uint32_t vslot[2] = {lds0 + 24576u, lds0 + 32768u};
+    auto kslot = [&](int i) -> uint32_t { return lds0 + 8192u * (uint32_t)i; };
 
     int h, j;
-    unit_of(blockIdx.x, a.H, a.N, a.n_t, a.n_v, a.n_a, h, j);
+    unit_of(blockIdx.x, a.H, a.n_t, a.n_v, a.n_a, h, j);
     if (h >= a.H || j >= a.N) return;  // not reached: the map is a bijection onto the units
     const int lane = threadIdx.x, g = lane >> 5, l32 = lane & 31;
     const int64_t rs = (int64_t)a.H * kD;  // elements between consecutive tokens
     const bool video = j >= a.n_t && j < a.n_t + a.n_v;
     const int u = j - a.n_t;
-    const int n_half = 2 * (video ? a.n_t + a.kk + a.n_a : a.N);
+    const int n_tiles = video ? a.n_t + a.kk + a.n_a : a.N;
     const int32_t* selrow = a.sel + ((int64_t)h * a.n_v + (video ? u : 0)) * a.kk;
     const float c2 = a.scale_log2;
 
-    // position `it` of this unit's ascending key-tile list -> tile index
+    // position `it` of this unit's ascending key-tile list -> tile index;
+    // positions past the end name the last tile
     auto tile_at = [&](int it) -> int {
+        if (it >= n_tiles) it = n_tiles - 1;
         if (!video || it < a.n_t) return it;
         if (it < a.n_t + a.kk) {
             // caller-supplied index sets are clamped into range, never followed out of bounds
@@ -244,9 +229,17 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
     // tensor, two 8 KiB half-tiles each
     const char* kbase = (const char*)(a.kpack + (int64_t)h * a.N * (kT * kD));
     const char* vbase = (const char*)(a.vpack + (int64_t)h * a.N * (kT * kD));
-    const uint32_t lane_off = 16u * lane;
     constexpr int64_t kTileBytes = 2 * kTileElems;
     constexpr int64_t kHalfBytes = 2 * kHalfElems;
+    uint32_t voff[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) voff[i] = 16u * lane + 1024u * i;
+    auto fetch_k = [&](uint32_t slot, int tile, int half) {
+        fetch_half(slot, kbase + tile * kTileBytes + half * kHalfBytes, voff);
+    };
+    auto fetch_v = [&](uint32_t slot, int tile, int half) {
+        fetch_half(slot, vbase + tile * kTileBytes + half * kHalfBytes, voff);
+    };
 
     // Q^T fragments (B operand of S^T = K Q^T): query l32 of block qb, dims 16s + 8g .. +7
     bf16x8 qf[2][8];
@@ -254,17 +247,15 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
     for (int qb = 0; qb < 2; ++qb) {
         const uint16_t* qp = a.q + ((int64_t)j * kT + 32 * qb + l32) * rs + (int64_t)h * kD + 8 * g;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) qf[qb][s] = *(const bf16x8*)(qp + 16 * s);
+        for (int s8 = 0; s8 < 8; ++s8) qf[qb][s8] = *(const bf16x8*)(qp + 16 * s8);
     }
     wait_vmcnt(0);  // Q is resident before the ring starts counting loads
 
-    const int n_tiles = n_half / 2;
-    const int first = tile_at(0);
-    const int second = n_tiles > 1 ? tile_at(1) : first;
+    const int t0 = tile_at(0), t1 = tile_at(1);
 
     // Softmax reference.  Each column uses one fixed reference m_ref (in units
-    // of scale_log2 * score) for its whole key list: P = 2^(x - m_ref) and
-    // O, l accumulate without any rescaling.  m_ref starts at the column max
+    // of scale_log2 * score) for its whole key list: P = 2^(x - m_ref), and O
+    // and l accumulate without any rescaling.  m_ref starts at the column max
     // of the first half-tile, so the largest P of that half-tile is 1.  If a
     // later score exceeds it by so much that the denominator passes 2^100 (or
     // overflows), the unit is recomputed with m_ref raised by log2 of the
@@ -273,83 +264,120 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
     float m_ref[2];
     f32x16 o[2][4];
     float l_run[2];
+    f32x16 zero16;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) zero16[i] = 0.0f;
+    bf16x8 zero8;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) zero8[i] = (__bf16)0.0f;
     for (int pass = 0;; ++pass) {
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             l_run[qb] = 0.0f;
 #pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) o[qb][db][i] = 0.0f;
+            for (int db = 0; db < 4; ++db) o[qb][db] = zero16;
         }
-        // cur / nxt: tile of the current half-tiles and the next list entry
-        // (past the end of the list both name the last tile, whose data is
-        // then fetched again and left unused: the loop body has no branches)
-        int cur = first, nxt = second;
-        // prologue: K(0), V(0), K(1) in that order, then S^T of half-tile 0
-        fetch_half(kslot[0], kbase + cur * kTileBytes, lane_off);
-        fetch_half(vslot[0], vbase + cur * kTileBytes, lane_off);
-        fetch_half(kslot[1], kbase + cur * kTileBytes + kHalfBytes, lane_off);
+        // Half-tile x of the list: K(x) and V(x) are half (x & 1) of tile
+        // (x >> 1), staged in K slot x mod 3 and V slot x mod 2.  Step x
+        // computes
+        //   S^T(x+1) = K(x+1) Q^T              (16 MFMAs)
+        //   P(x)     = numerators of S^T(x)     (vector ALU)
+        //   O       += V(x-1) P(x-1)            (16 MFMAs)
+        // so none of its matrix work waits for its own vector work.  Operands
+        // enter registers one step ahead (K(x+2) in the middle of step x,
+        // V(x) at its end).  Step x fetches V(x+1) and then K(x+4), so a K
+        // half-tile has two and a half steps to arrive and a V half-tile two.
+        // In issue order, everything up to K(x+2) is complete once at most 32
+        // fetches are outstanding (V(x), K(x+3) of step x-1 and this step's
+        // two), and everything up to V(x) once at most 24 are.
+        bf16x8 kop[8], vop[8];
+        bf16x8 pprev[2][2];
+        f32x16 sc[2];
+        // prologue: K(0), K(1), K(2); S^T(0); then V(0), K(3) as the fetches
+        // of step -1; PV(-1) multiplies zeros
+        fetch_k(kslot(0), t0, 0);
+        fetch_k(kslot(1), t0, 1);
+        fetch_k(kslot(2), t1, 0);
         wait_vmcnt(16);
-        f32x16 sacc[2][2];  // [parity of the half-tile][query block]
-        sacc[0][0] = qk_block((const bf16x8*)kslot[0] + lane, qf[0]);
-        sacc[0][1] = qk_block((const bf16x8*)kslot[0] + lane, qf[1]);
+        read_ops(kop, kslot(0), lane);
+        sc[0] = zero16;
+        sc[1] = zero16;
+#pragma unroll
+        for (int s8 = 0; s8 < 8; ++s8) {
+            sc[0] = mfma32(kop[s8], qf[0][s8], sc[0]);
+            sc[1] = mfma32(kop[s8], qf[1][s8], sc[1]);
+        }
+        wait_vmcnt(8);
+        wait_lgkm();
+        read_ops(kop, kslot(1), lane);
+        fetch_v(vslot[0], t0, 0);
+        fetch_k(kslot(0), t1, 1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vop[i] = zero8;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) pprev[qb][0] = pprev[qb][1] = zero8;
         if (pass == 0) {
-            m_ref[0] = column_max(sacc[0][0], c2);
-            m_ref[1] = column_max(sacc[0][1], c2);
+            m_ref[0] = column_max(sc[0], c2);
+            m_ref[1] = column_max(sc[1], c2);
         }
 
-        // Step h (half-tile h, parity pp): fetch V(h+1) and K(h+2); wait for
-        // K(h+1) and V(h) (issued one step earlier); then, without branches:
-        //   S^T(h+1) (16 MFMAs)      alongside  numerators(h, block 0)
-        //   O[0] += V(h) P(h, 0)     alongside  numerators(h, block 1)
-        //   O[1] += V(h) P(h, 1)
-        // Issue order keeps "everything up to K(h+1)" = "all but this step's
-        // 16 fetches", so one vmcnt(16) wait serves every step.
+        // tiles of list positions t, t+1 (cur, nxt) carried across iterations;
+        // xm3 = x mod 3 for the current step x
+        int cur = t0, nxt = t1;
+        int xm3 = 0;
         for (int t = 0; t < n_tiles; ++t) {
-            const int nn = t + 2 < n_tiles ? tile_at(t + 2) : nxt;
+            const int nn = tile_at(t + 2);
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
-                asm volatile("" ::: "memory");
-                const int tile_v = pp == 0 ? cur : nxt;  // V(h+1): (t, half 1) or (t+1, half 0)
-                fetch_half(vslot[pp ^ 1], vbase + tile_v * kTileBytes + (pp ^ 1) * kHalfBytes, lane_off);
-                fetch_half(kslot[pp], kbase + nxt * kTileBytes + pp * kHalfBytes, lane_off);  // K(h+2)
-                wait_vmcnt(16);
-                const bf16x8* ks = (const bf16x8*)kslot[pp ^ 1] + lane;
-                const bf16x8* vs = (const bf16x8*)vslot[pp] + lane;
-                bf16x8 kop[8];
-#pragma unroll
-                for (int s8 = 0; s8 < 8; ++s8) kop[s8] = ks[s8 * 64];
-                f32x16 n0, n1;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) { n0[i] = 0.0f; n1[i] = 0.0f; }
-                bf16x8 p0[2], p1[2];
+                // step x = 2t + pp
+                const int k_wr = xm3 == 2 ? 0 : xm3 + 1;  // (x + 4) mod 3
+                const int k_rd = xm3 == 0 ? 2 : xm3 - 1;  // (x + 2) mod 3
+                wait_lgkm();  // kop = K(x+1), vop = V(x-1)
+                // V(x+1): (t, half 1) or (t+1, half 0); K(x+4): (t+2, half pp)
+                fetch_v(vslot[pp ^ 1], pp == 0 ? cur : nxt, pp ^ 1);
+                fetch_k(kslot(k_wr), nn, pp);
+                f32x16 n0 = zero16, n1 = zero16;
+                bf16x8 pc[2][2];
 #pragma unroll
                 for (int s8 = 0; s8 < 8; ++s8) {
                     n0 = mfma32(kop[s8], qf[0][s8], n0);
                     n1 = mfma32(kop[s8], qf[1][s8], n1);
                 }
-                numerators(sacc[pp][0], c2, m_ref[0], l_run[0], p0[0], p0[1]);
-                bf16x8 vop[8];
-#pragma unroll
-                for (int m8 = 0; m8 < 8; ++m8) vop[m8] = vs[m8 * 64];
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) o[0][db] = mfma32(vop[2 * db + m], p0[m], o[0][db]);
-                numerators(sacc[pp][1], c2, m_ref[1], l_run[1], p1[0], p1[1]);
+                numerators(sc[0], c2, m_ref[0], l_run[0], pc[0][0], pc[0][1]);
+                wait_vmcnt(32);  // K(x+2)
+                read_ops(kop, kslot(k_rd), lane);
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
 #pragma unroll
-                    for (int m = 0; m < 2; ++m) o[1][db] = mfma32(vop[2 * db + m], p1[m], o[1][db]);
-                sacc[pp ^ 1][0] = n0;
-                sacc[pp ^ 1][1] = n1;
+                    for (int m = 0; m < 2; ++m) {
+                        o[0][db] = mfma32(vop[2 * db + m], pprev[0][m], o[0][db]);
+                        o[1][db] = mfma32(vop[2 * db + m], pprev[1][m], o[1][db]);
+                    }
+                numerators(sc[1], c2, m_ref[1], l_run[1], pc[1][0], pc[1][1]);
+                wait_vmcnt(24);  // V(x)
+                read_ops(vop, vslot[pp], lane);
+                sc[0] = n0;
+                sc[1] = n1;
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    pprev[qb][0] = pc[qb][0];
+                    pprev[qb][1] = pc[qb][1];
+                }
+                xm3 = k_wr;  // (x + 1) mod 3
             }
             cur = nxt;
             nxt = nn;
         }
+        // the last PV
+        wait_lgkm();
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                o[0][db] = mfma32(vop[2 * db + m], pprev[0][m], o[0][db]);
+                o[1][db] = mfma32(vop[2 * db + m], pprev[1][m], o[1][db]);
+            }
         wait_vmcnt(0);
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         l_run[0] = xhalf_sum(l_run[0]);
         l_run[1] = xhalf_sum(l_run[1]);
         const bool big0 = !(l_run[0] <= 0x1p100f), big1 = !(l_run[1] <= 0x1p100f);
