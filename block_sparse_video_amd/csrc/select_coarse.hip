@@ -36,7 +36,63 @@ __device__ __forceinline__ uint64_t order_key(double x) {
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-template <int R>
+// Exact k-th largest of one row's keys by bisection on the 64-bit key value,
+// one wavefront per row, the row's keys held in registers (lane l owns
+// columns l, l + 64, ...; NS slots, n_v <= 64 * NS).  count(T) = number of
+// keys >= T is taken with one ballot per slot.  Invariant: count(lo) >= k >
+// count(hi).  A probe with count exactly k ends the search early (the keys >=
+// it are the selection); otherwise lo ends at the k-th largest key.  Returns
+// T and sets `need` = k - #(keys > T), the number of keys equal to T to take.
+template <int NS>
+__device__ __forceinline__ uint64_t kth_key_bisect(const double* row, int n_v, int k, int lane,
+                                                   uint32_t& need) {
+    uint64_t kv[NS];
+    uint64_t kmin = ~0ull, kmax = 0ull;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int w = lane + 64 * i;
+        kv[i] = w < n_v ? order_key(row[w]) : 0ull;  // finite scores never map to 0
+        if (w < n_v) {
+            kmin = kv[i] < kmin ? kv[i] : kmin;
+            kmax = kv[i] > kmax ? kv[i] : kmax;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t a = __shfl_xor(kmin, off), b = __shfl_xor(kmax, off);
+        kmin = a < kmin ? a : kmin;
+        kmax = b > kmax ? b : kmax;
+    }
+    // every lane now holds the row's min and max; make them wave-uniform
+    kmin = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(kmin >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kmin);
+    kmax = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(kmax >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)kmax);
+    auto count_ge = [&](uint64_t t) -> uint32_t {
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) c += (uint32_t)__popcll(__ballot(kv[i] >= t));
+        return c;
+    };
+    uint64_t lo = kmin, hi = kmax + 1;  // count(kmin) = n_v >= k; count(kmax + 1) = 0 < k
+    while (hi - lo > 1) {
+        const uint64_t mid = lo + ((hi - lo) >> 1);
+        const uint32_t c = count_ge(mid);
+        if (c >= (uint32_t)k) {
+            lo = mid;
+            if (c == (uint32_t)k) break;
+        } else {
+            hi = mid;
+        }
+    }
+    uint32_t gt = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) gt += (uint32_t)__popcll(__ballot(kv[i] > lo));
+    need = (uint32_t)k - gt;
+    return lo;
+}
+
+template <int R, int NS>
 __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __restrict__ qbar64,
                                                             const float* __restrict__ kbar_t,
                                                             const float* __restrict__ vbar, int n_v,
@@ -88,63 +144,69 @@ __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __rest
         const int r = wv + 4 * t;
         const bool active = (r < R) && (u0 + r < n_v);
         const double* row = sc + min(r, R - 1) * ldw;
-        uint64_t prefix = 0, mask = 0;
+        uint64_t prefix = 0;
         uint32_t remaining = (uint32_t)k;
-        for (int shift = 56; shift >= 0; shift -= 8) {
-            if (active)
-                for (int i = lane; i < 256; i += 64) hist[i] = 0u;
-            __syncthreads();
-            if (active) {
-                for (int w = lane; w < n_v; w += 64) {
-                    const uint64_t key = order_key(row[w]);
-                    if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        if constexpr (NS > 0) {
+            if (active) prefix = kth_key_bisect<NS>(row, n_v, k, lane, remaining);
+        } else {
+            uint64_t mask = 0;
+            for (int shift = 56; shift >= 0; shift -= 8) {
+                if (active)
+                    for (int i = lane; i < 256; i += 64) hist[i] = 0u;
+                __syncthreads();
+                if (active) {
+                    for (int w = lane; w < n_v; w += 64) {
+                        const uint64_t key = order_key(row[w]);
+                        if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+                    }
                 }
-            }
-            __syncthreads();
-            if (active) {
-                // lane i owns bins 255-4i .. 252-4i (descending)
-                const uint32_t c0 = hist[255 - 4 * lane], c1 = hist[254 - 4 * lane];
-                const uint32_t c2 = hist[253 - 4 * lane], c3 = hist[252 - 4 * lane];
-                const uint32_t tot = c0 + c1 + c2 + c3;
-                uint32_t incl = tot;
-#pragma unroll
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t y = __shfl_up(incl, off);
-                    if (lane >= off) incl += y;
-                }
-                const uint32_t excl = incl - tot;
-                const bool hit = excl < remaining && remaining <= incl;
-                const uint64_t hb = __ballot(hit);
-                const int src = __ffsll((long long)hb) - 1;
-                int digit = 0;
-                uint32_t above = 0;
-                if (hit) {
-                    uint32_t cum = excl;
-                    if (cum + c0 >= remaining) {
-                        digit = 255 - 4 * lane;
-                    } else {
-                        cum += c0;
-                        if (cum + c1 >= remaining) {
-                            digit = 254 - 4 * lane;
+                __syncthreads();
+                if (active) {
+                    // lane i owns bins 255-4i .. 252-4i (descending)
+                    const uint32_t c0 = hist[255 - 4 * lane], c1 = hist[254 - 4 * lane];
+                    const uint32_t c2 = hist[253 - 4 * lane], c3 = hist[252 - 4 * lane];
+                    const uint32_t tot = c0 + c1 + c2 + c3;
+                    uint32_t incl = tot;
+    #pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const uint32_t y = __shfl_up(incl, off);
+                        if (lane >= off) incl += y;
+                    }
+                    const uint32_t excl = incl - tot;
+                    const bool hit = excl < remaining && remaining <= incl;
+                    const uint64_t hb = __ballot(hit);
+                    const int src = __ffsll((long long)hb) - 1;
+                    int digit = 0;
+                    uint32_t above = 0;
+                    if (hit) {
+                        uint32_t cum = excl;
+                        if (cum + c0 >= remaining) {
+                            digit = 255 - 4 * lane;
                         } else {
-                            cum += c1;
-                            if (cum + c2 >= remaining) {
-                                digit = 253 - 4 * lane;
+                            cum += c0;
+                            if (cum + c1 >= remaining) {
+                                digit = 254 - 4 * lane;
                             } else {
-                                cum += c2;
-                                digit = 252 - 4 * lane;
+                                cum += c1;
+                                if (cum + c2 >= remaining) {
+                                    digit = 253 - 4 * lane;
+                                } else {
+                                    cum += c2;
+                                    digit = 252 - 4 * lane;
+                                }
                             }
                         }
+                        above = cum;
                     }
-                    above = cum;
+                    digit = __shfl(digit, src);
+                    above = __shfl(above, src);
+                    prefix |= (uint64_t)digit << shift;
+                    mask |= 255ull << shift;
+                    remaining -= above;
                 }
-                digit = __shfl(digit, src);
-                above = __shfl(above, src);
-                prefix |= (uint64_t)digit << shift;
-                mask |= 255ull << shift;
-                remaining -= above;
+                __syncthreads();
             }
-            __syncthreads();
+
         }
         if (active) {
             // prefix = the k-th largest key T; take every key > T and the
@@ -178,6 +240,7 @@ __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __rest
                 wrow[w] = (double)p;
                 lsum += (double)p;
             }
+            for (int w = n_v + lane; w < ldw; w += 64) wrow[w] = 0.0;  // pad: weight 0
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
             if (lane == 0) rowsum[r] = lsum;
@@ -186,6 +249,10 @@ __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __rest
     __syncthreads();
 
     // ---- coarse output: c[u][d] = sum_w p_w Vbar[w][d] / sum_w p_w --------
+    // thread (d, half) accumulates rows half*RH .. half*RH + RH - 1; pooled V
+    // values are requested 32 columns at a time and the weights of two
+    // columns come in one LDS read (rows are padded with zero weights to a
+    // multiple of 32 columns)
     constexpr int RH = (R + 1) / 2;
     const int d = tid & 127;
     const int half = tid >> 7;
@@ -193,14 +260,22 @@ __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __rest
 #pragma unroll
     for (int i = 0; i < RH; ++i) acc[i] = 0.0;
     const float* vb = vbar + (int64_t)h * n_v * kD + d;
-    int rr_row[RH];
+    const double* prow[RH];
 #pragma unroll
-    for (int i = 0; i < RH; ++i) rr_row[i] = min(half * RH + i, R - 1);
-#pragma unroll 4
-    for (int w = 0; w < n_v; ++w) {
-        const double vd = (double)vb[(int64_t)w * kD];
+    for (int i = 0; i < RH; ++i) prow[i] = sc + min(half * RH + i, R - 1) * ldw;
+    for (int w0 = 0; w0 < n_v; w0 += 32) {
+        float vr[32];
 #pragma unroll
-        for (int i = 0; i < RH; ++i) acc[i] = __fma_rn(sc[rr_row[i] * ldw + w], vd, acc[i]);
+        for (int i = 0; i < 32; ++i) vr[i] = vb[(int64_t)min(w0 + i, n_v - 1) * kD];
+#pragma unroll
+        for (int i = 0; i < 32; i += 2) {
+#pragma unroll
+            for (int r = 0; r < RH; ++r) {
+                const double2 p2 = *(const double2*)(prow[r] + w0 + i);
+                acc[r] = __fma_rn(p2.x, (double)vr[i], acc[r]);
+                acc[r] = __fma_rn(p2.y, (double)vr[i + 1], acc[r]);
+            }
+        }
     }
 #pragma unroll
     for (int i = 0; i < RH; ++i) {
@@ -210,20 +285,20 @@ __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __rest
     }
 }
 
-template <int R>
+template <int R, int NS>
 hipError_t launch_r(const Shape& s, int32_t* sel, uint8_t* ws, const Layout& L, hipStream_t stream,
                     int ldw, size_t lds) {
     // Raise the kernel's dynamic-LDS limit when a larger row pitch needs it.
     static std::atomic<size_t> lds_allowed{0};
     if (lds > lds_allowed.load()) {
-        hipError_t e = hipFuncSetAttribute((const void*)select_coarse_kernel<R>,
+        hipError_t e = hipFuncSetAttribute((const void*)select_coarse_kernel<R, NS>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         lds_allowed.store(lds);
     }
     dim3 grid((s.n_v + R - 1) / R, s.H);
     const float alpha = (float)(1.0 / 11.313708498984761);  // 1/sqrt(128)
-    hipLaunchKernelGGL(select_coarse_kernel<R>, grid, dim3(256), lds, stream,
+    hipLaunchKernelGGL((select_coarse_kernel<R, NS>), grid, dim3(256), lds, stream,
                        (const double*)(ws + L.qbar64), (const float*)(ws + L.kbar_t),
                        (const float*)(ws + L.vbar), s.n_v, s.k, ldw, alpha, sel,
                        (float*)(ws + L.coarse));
@@ -239,14 +314,18 @@ size_t select_lds_bytes(int R, int ldw) { return (size_t)R * ldw * 8 + 4 * 256 *
 
 hipError_t launch_select_coarse(const Shape& s, int32_t* sel, uint8_t* ws, const Layout& L,
                                 hipStream_t stream) {
-    const int ldw = (s.n_v + 1) & ~1;
+    const int ldw = (s.n_v + 31) & ~31;  // row pitch: whole groups of 32 columns
+    // rows of up to 64 * 20 keys are selected from registers, longer rows by
+    // the LDS radix select
+    if (s.n_v <= 64 * 20 && select_lds_bytes(8, ldw) <= kSelectLdsMax / 2)
+        return launch_r<8, 20>(s, sel, ws, L, stream, ldw, select_lds_bytes(8, ldw));
     if (select_lds_bytes(8, ldw) <= kSelectLdsMax / 2)
-        return launch_r<8>(s, sel, ws, L, stream, ldw, select_lds_bytes(8, ldw));
+        return launch_r<8, 0>(s, sel, ws, L, stream, ldw, select_lds_bytes(8, ldw));
     if (select_lds_bytes(4, ldw) <= kSelectLdsMax / 2)
-        return launch_r<4>(s, sel, ws, L, stream, ldw, select_lds_bytes(4, ldw));
+        return launch_r<4, 0>(s, sel, ws, L, stream, ldw, select_lds_bytes(4, ldw));
     if (select_lds_bytes(2, ldw) <= kSelectLdsMax)
-        return launch_r<2>(s, sel, ws, L, stream, ldw, select_lds_bytes(2, ldw));
-    return launch_r<1>(s, sel, ws, L, stream, ldw, select_lds_bytes(1, ldw));
+        return launch_r<2, 0>(s, sel, ws, L, stream, ldw, select_lds_bytes(2, ldw));
+    return launch_r<1, 0>(s, sel, ws, L, stream, ldw, select_lds_bytes(1, ldw));
 }
 
 }  // namespace vsa

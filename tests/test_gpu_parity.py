@@ -151,6 +151,43 @@ def test_zero_query_ties_and_duplicate_keys():
     full_check(dict(x, k=kdup), s_t, s_v, s_a, 0.2, exempt_ok=False)
 
 
+def test_paired_key_tiles_tie_at_the_boundary():
+    """K tiles equal in pairs: every score is tied with exactly one other, so
+    with k odd the k-th and (k+1)-th largest scores tie in every row and the
+    lower index must win.  Selection must match the oracle exactly."""
+    announce("paired K tiles: h=2 tiles=(1,70,1) frac=0.3 (k=21)")
+    h, s_t, n_v, s_a = 2, 64, 70, 64
+    s_v = n_v * T
+    x = synth.vsa_inputs(16, h, s_t, s_v, s_a)
+    kp = x["k"].copy()
+    for w in range(0, n_v, 2):
+        a = s_t + w * T
+        kp[a + T: a + 2 * T] = kp[a: a + T]
+    ref, *_ = full_check(dict(x, k=kp), s_t, s_v, s_a, 0.3, exempt_ok=False)
+    assert ref["k"] == 21
+
+
+@pytest.mark.slow
+def test_long_rows_use_the_radix_select():
+    """n_v = 1,300 video tiles: rows too long for the register bisection go
+    through the LDS radix select.  Every selection row and the coarse branch
+    are checked; outputs on sampled rows."""
+    h, s_t, s_v, s_a = 2, 64, 64 * 1300, 64
+    announce(f"long rows: h={h} ({s_t},{s_v},{s_a}) k={bsv.vsa_topk_count(s_v, 0.2)}")
+    x = synth.vsa_inputs(17, h, s_t, s_v, s_a, threads=THREADS)
+    xd = G.inputs_to_dev(x)
+    out, sel, ws = G.run_forward(xd, s_t, s_v, s_a, 0.2)
+    ref = oracle.select_coarse(x["q"], x["k"], x["v"], s_t, s_v, s_a, 0.2, threads=THREADS)
+    got_sel = sel.cpu().numpy()
+    G.check_selection(got_sel, ref)
+    w = G.read_workspace(ws, h, s_t, s_v, s_a)
+    np.testing.assert_allclose(w["coarse"], ref["coarse"], rtol=2e-5, atol=2e-7)
+    rows = G.sample_rows(s_t, s_v, s_a, n_video_tiles=3, per_tile=(0, 37, 63))
+    _, ref_out = oracle.fine(x["q"], x["k"], x["v"], x["gate"], s_t, s_v, s_a, got_sel,
+                             ref["coarse"], rows, threads=THREADS)
+    G.assert_outputs_close(G.from_dev_bits(out)[rows], ref_out)
+
+
 def test_designed_ranking():
     announce("designed ranking")
     h, s_t, n_v = 1, 64, 15
