@@ -10,7 +10,9 @@ over synthetic seeded inputs already resident in HBM.  Default workload: the
 Prints ONE JSON line.  value = effective TFLOP/s on computed tiles only
 (QK^T and PV of every computed 64x64 tile pair, 4*64*64*128 FLOP each);
 ms_per_step = ms per layer.  A 14-head run of the same shape (heads 0-13 of
-the same tensors, one SP4 rank's share) is reported under "secondary".
+the same tensors, one SP4 rank's share) is reported under "secondary", and
+the whole attention layer (Q/K/V/gate projections of smooth-field hidden
+states, then the VSA forward) under "full_layer".
 """
 from __future__ import annotations
 
@@ -126,6 +128,64 @@ def time_path(bsv, torch, xd, shape, frac, steps, warmup):
             "out": out, "sel": sel}
 
 
+FULL_LAYER = dict(text_len=1024, grid=(18, 48, 84), audio_len=1024, hidden=5376, heads=56)
+
+
+def full_layer(bsv, torch, np, frac, steps, warmup, threads):
+    """The whole attention layer on the 10 s shape: hidden states x [74,624 x 5,376]
+    (text/audio rows iid N(0,1), video rows smooth 3D Gaussian fields over the
+    18 x 48 x 84 latent grid, tile-packed), projections to Q/K/V/gate
+    (weights N(0, 0.02^2)), then the VSA forward.  HIP events around each
+    stage on the launch stream."""
+    import synth
+    print("[bench] full layer: generating inputs", file=sys.stderr, flush=True)
+    d = synth.full_layer_inputs(0, threads=threads, **FULL_LAYER)
+    h, s_t, s_a, hidden = FULL_LAYER["heads"], FULL_LAYER["text_len"], FULL_LAYER["audio_len"], FULL_LAYER["hidden"]
+    tokens = d["x"].shape[0]
+    s_v = tokens - s_t - s_a
+    x = torch.from_numpy(d["x"].view(np.int16)).to("cuda").view(torch.bfloat16)
+    w = torch.from_numpy(d["w"].view(np.int16)).to("cuda").view(torch.bfloat16)
+    del d
+    qkvg = [torch.empty((tokens, h, D), dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    out, sel, ws = bsv.alloc_outputs(h, s_t, s_v, s_a, frac)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        bsv.vsa_project_qkvg(x, w, h, *qkvg)
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        bsv.vsa_forward(*qkvg, s_t, s_v, s_a, frac, out, sel, ws)
+        return e
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    print("[bench] full layer: timing", file=sys.stderr, flush=True)
+    marks = []
+    for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        em = step()
+        e1 = torch.cuda.Event(enable_timing=True)
+        e1.record(stream)
+        marks.append((e0, em, e1))
+    torch.cuda.synchronize()
+    gemm_ms = sum(a.elapsed_time(b) for a, b, _ in marks) / steps
+    vsa_ms = sum(b.elapsed_time(c) for _, b, c in marks) / steps
+    kk = bsv.vsa_topk_count(s_v, frac)
+    gemm_flops = 2.0 * tokens * hidden * h * D * 4
+    vsa_flops = tile_pairs(h, s_t, s_v, s_a, kk) * FLOP_PER_PAIR
+    layer_ms = gemm_ms + vsa_ms
+    return {"workload": "full layer, 10 s shape: x[74,624 x 5,376] -> Q/K/V/gate (56 x 128 each) "
+                        "-> VSA; video rows smooth fields (sigma 1, 2, 2 cells), k=227",
+            "ms_per_layer": layer_ms, "projection_ms": gemm_ms, "vsa_ms": vsa_ms,
+            "projection_tflops": gemm_flops / (gemm_ms * 1e-3) / 1e12,
+            "projection_frac": gemm_flops / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "vsa_tflops": vsa_flops / (vsa_ms * 1e-3) / 1e12,
+            "layer_tflops": (gemm_flops + vsa_flops) / (layer_ms * 1e-3) / 1e12,
+            "steps": steps}
+
+
 def cpu_baseline(x, shape, frac, budget_rows, threads):
     """The oracle (untuned) on a bounded sample: selection + coarse for every
     row, the fine branch for a stratified sample of query rows."""
@@ -173,6 +233,8 @@ def main():
     ap.add_argument("--topk-frac", type=float, default=0.2)
     ap.add_argument("--no-secondary", action="store_true", help="skip the 14-head run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-full-layer", action="store_true",
+                    help="skip the full-layer run (Q/K/V/gate projections + VSA on smooth video fields)")
     ap.add_argument("--cpu-rows", type=int, default=48, help="video tiles in the oracle sample")
     ap.add_argument("--threads", type=int, default=None, help="oracle / generator threads")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -264,6 +326,8 @@ def main():
                                "fine_attn_ms": r14["stage_ms"][2],
                                "fine_frac": f14 / (r14["stage_ms"][2] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         del x14, r14
+    if not args.no_full_layer and args.workload == "10s_56h":
+        result["full_layer"] = full_layer(bsv, torch, np, frac, max(3, args.steps // 4), 2, threads)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(x, shape, frac, args.cpu_rows, threads)

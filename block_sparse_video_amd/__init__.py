@@ -152,3 +152,30 @@ def forward(q, k, v, gate, text_len, video_len, audio_len, topk_frac=0.2, worksp
     vsa_forward(q, k, v, gate, text_len, video_len, audio_len, topk_frac, out, sel,
                 workspace if workspace is not None else ws, stream)
     return out, sel
+
+
+def vsa_project_qkvg(x, w, num_heads, q, k, v, gate, stream=None):
+    """Q/K/V/gate projections: x bf16 [tokens][hidden], w bf16
+    [4][num_heads*128][hidden] (q, k, v, gate weights, each out x in); writes
+    q, k, v, gate bf16 [tokens][num_heads][128]."""
+    torch = _torch()
+    x = _tensor(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be [tokens][hidden]")
+    tokens, hidden = x.shape
+    w = _tensor(w, "w", torch.bfloat16, (4, num_heads * HEAD_DIM, hidden))
+    outs = [_tensor(t, n, torch.bfloat16, (tokens, num_heads, HEAD_DIM))
+            for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"))]
+    _check(load().vsa_project_qkvg(_ptr(x), _ptr(w), tokens, hidden, num_heads,
+                                   *[_ptr(t) for t in outs], _stream(stream)),
+           "vsa_project_qkvg")
+
+
+def project_qkvg(x, w, num_heads, stream=None):
+    """Convenience wrapper: allocates the four outputs with torch and calls
+    vsa_project_qkvg."""
+    torch = _torch()
+    outs = [torch.empty((x.shape[0], num_heads, HEAD_DIM), dtype=torch.bfloat16, device=x.device)
+            for _ in range(4)]
+    vsa_project_qkvg(x, w, num_heads, *outs, stream=stream)
+    return tuple(outs)

@@ -24,6 +24,7 @@ SIGNATURES = {
     "vsa_pool_pack": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I64, _I64, _P, _SZ, _P]),
     "vsa_select_coarse": (ctypes.c_int, [_I32, _I64, _I64, _I64, _F32, _P, _P, _SZ, _P]),
     "vsa_fine_attention": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _F32, _P, _P, _P, _SZ, _P]),
+    "vsa_project_qkvg": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P]),
 }
 
 _lib = None

@@ -241,4 +241,23 @@ vsa_status vsa_forward(const void* q, const void* k, const void* v, const void* 
     return from_hip(e);
 }
 
+vsa_status vsa_project_qkvg(const void* x, const void* w, int64_t tokens, int32_t hidden,
+                            int32_t num_heads, void* q, void* k, void* v, void* gate,
+                            void* stream) {
+    if (!x || !w || !q || !k || !v || !gate) return VSA_ERR_NULL_POINTER;
+    if (tokens < 1 || hidden < 64 || num_heads < 2) return VSA_ERR_BAD_SHAPE;
+    if (hidden % 64 || num_heads % 2) return VSA_ERR_UNALIGNED_LENGTH;
+    if (hidden > 16384 || num_heads > VSA_MAX_HEADS || tokens > VSA_MAX_TOKENS)
+        return VSA_ERR_TOO_LARGE;
+    if (!aligned(x, 16) || !aligned(w, 16) || !aligned(q, 16) || !aligned(k, 16) ||
+        !aligned(v, 16) || !aligned(gate, 16))
+        return VSA_ERR_MISALIGNED;
+    vsa_status st = check_device();
+    if (st != VSA_OK) return st;
+    uint16_t* const outs[4] = {(uint16_t*)q, (uint16_t*)k, (uint16_t*)v, (uint16_t*)gate};
+    return from_hip(vsa::launch_project_qkvg((const uint16_t*)x, (const uint16_t*)w, outs, tokens,
+                                             hidden, num_heads * VSA_HEAD_DIM,
+                                             (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -55,4 +55,7 @@ hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate,
                                  const int32_t* sel, uint16_t* out, const Shape& s,
                                  const uint8_t* ws, const Layout& L, hipStream_t stream);
 
+hipError_t launch_project_qkvg(const uint16_t* x, const uint16_t* w, uint16_t* const out[4],
+                               int64_t tokens, int hidden, int n_out, hipStream_t stream);
+
 }  // namespace vsa

@@ -145,6 +145,25 @@ vsa_status vsa_fine_attention(const void* q, const void* gate, int32_t num_heads
                               float topk_frac, const int32_t* selected_tiles, void* out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* The Q, K, V and gate projections that produce this path's inputs (page
+ * "UniServe: serving FastH3 at its fastest", section "The FastH3 workload":
+ * hidden size 5,376, 56 heads of 128, so each projection maps 5,376 channels
+ * to 7,168):
+ *   out_p[s][n] = sum_c x[s][c] * w[p][n][c]    for p = 0 (q), 1 (k), 2 (v), 3 (gate)
+ * with fp32 accumulation and each result rounded to bf16 (nearest even).
+ *   x        bf16 [tokens][hidden], row-major
+ *   w        bf16 [4][num_heads * 128][hidden]: the four weight matrices,
+ *            each out x in (row n = output channel n)
+ *   q, k, v, gate   bf16 [tokens][num_heads][128] outputs, the layout
+ *            vsa_forward reads
+ * Requirements: tokens >= 1; hidden a multiple of 64 and at most 16384;
+ * num_heads even (num_heads * 128 a multiple of 256) and at most
+ * VSA_MAX_HEADS; every pointer 16-byte aligned; tokens <= VSA_MAX_TOKENS.
+ * No workspace.  Asynchronous on `stream`, like vsa_forward. */
+vsa_status vsa_project_qkvg(const void* x, const void* w, int64_t tokens, int32_t hidden,
+                            int32_t num_heads, void* q, void* k, void* v, void* gate,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -171,3 +171,24 @@ def forward(q, k, v, gate, text_len, video_len, audio_len, frac, rows=None, thre
                         rows, threads=threads)
     sc.update({"rows": np.asarray(rows), "out": out_b, "out_f64": out_d})
     return sc
+
+
+def project_rows(x: np.ndarray, w: np.ndarray, rows) -> np.ndarray:
+    """The Q, K, V and gate projections of selected token rows, float64:
+    out[p][i][n] = sum over c of x[rows[i]][c] * w[p][n][c].
+
+    Page "UniServe: serving FastH3 at its fastest", section "The FastH3
+    workload": hidden size 5,376 and 56 heads of 128, so each projection maps
+    5,376 channels to 7,168 (weights stored out x in).  x is bfloat16 bits
+    [tokens][hidden], w bfloat16 bits [4][out][hidden]; both are widened
+    exactly to float64 and multiplied with numpy's matrix product (every
+    product of two bfloat16 values is exact in float64).  Returns float64
+    [4][len(rows)][out]; the GPU result is this value rounded to bfloat16
+    after fp32 accumulation."""
+    rows = np.asarray(rows, dtype=np.int64)
+    xr = (x[rows].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    out = np.empty((4, len(rows), w.shape[1]), dtype=np.float64)
+    for p in range(4):
+        wp = (w[p].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        out[p] = xr @ wp.T
+    return out

@@ -20,6 +20,7 @@
  */
 #include <math.h>
 #include <pthread.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -133,3 +134,117 @@ void synth_normal_f64(uint64_t seed, uint64_t stream, uint64_t offset, uint64_t 
 
 /* Raw 64-bit counter output, for tests of the generator itself. */
 uint64_t synth_splitmix64(uint64_t x) { return splitmix64(x); }
+
+/*
+ * Smooth video field (the full-layer workload's video rows): for every
+ * channel c of a T x Hh x Ww latent grid,
+ *   white noise   z[t][h][w] = normal deviate of element ((t*Hh + h)*Ww + w)*C + c
+ *                 of stream `stream` (same definition as above);
+ *   blur          a separable Gaussian filter, standard deviations (st, sh, sw)
+ *                 grid cells, weights exp(-i^2 / (2 s^2)) for |i| <= ceil(3 s),
+ *                 normalised to sum 1, half-sample symmetric boundary
+ *                 (x[-1] = x[0], x[-2] = x[1], ...), applied along t, then h, then w;
+ *   normalise     divided by the root mean square of the channel over the grid;
+ * rounded to bfloat16 and written in tile-packed token order: tiles of
+ * pt x ph x pw grid points in raster order over the tile grid, points in
+ * raster order inside a tile.  Grid point (t, h, w) goes to row
+ *   ((t/pt * (Hh/ph) + h/ph) * (Ww/pw) + w/pw) * (pt*ph*pw) + ((t%pt)*ph + h%ph)*pw + w%pw
+ * of `out` (row stride ld elements).  Hh, Ww, T must be multiples of ph, pw, pt.
+ */
+typedef struct {
+    uint64_t key;
+    int T, Hh, Ww, C, pt, ph, pw, c_begin, c_end;
+    double st, sh, sw;
+    uint16_t* out;
+    int64_t ld;
+} field_job_t;
+
+static int gauss_weights(double s, double* w) {
+    int R = (int)ceil(3.0 * s);
+    double sum = 0.0;
+    for (int i = -R; i <= R; ++i) sum += (w[i + R] = exp(-(double)(i * i) / (2.0 * s * s)));
+    for (int i = 0; i <= 2 * R; ++i) w[i] /= sum;
+    return R;
+}
+
+static inline int reflect_index(int i, int n) {
+    /* half-sample symmetric: ... 1 0 | 0 1 ... n-1 | n-1 n-2 ... */
+    int period = 2 * n;
+    i %= period;
+    if (i < 0) i += period;
+    return i < n ? i : period - 1 - i;
+}
+
+/* blur one channel block along one axis: n points, stride between points,
+   `lines` lines starting at line_start(k) */
+static void* run_field(void* p) {
+    field_job_t* j = (field_job_t*)p;
+    const int T = j->T, Hh = j->Hh, Ww = j->Ww, C = j->C;
+    const int64_t G = (int64_t)T * Hh * Ww;
+    double wt[64], wh[64], ww[64];
+    const int Rt = gauss_weights(j->st, wt), Rh = gauss_weights(j->sh, wh), Rw = gauss_weights(j->sw, ww);
+    double* a = (double*)malloc(sizeof(double) * G);
+    double* b = (double*)malloc(sizeof(double) * G);
+    for (int c = j->c_begin; c < j->c_end; ++c) {
+        for (int64_t g = 0; g < G; ++g) a[g] = normal_at(j->key, (uint64_t)(g * C + c));
+        /* along t */
+        for (int t = 0; t < T; ++t)
+            for (int hw = 0; hw < Hh * Ww; ++hw) {
+                double s = 0.0;
+                for (int i = -Rt; i <= Rt; ++i) s += wt[i + Rt] * a[(int64_t)reflect_index(t + i, T) * Hh * Ww + hw];
+                b[(int64_t)t * Hh * Ww + hw] = s;
+            }
+        /* along h */
+        for (int t = 0; t < T; ++t)
+            for (int h = 0; h < Hh; ++h)
+                for (int w = 0; w < Ww; ++w) {
+                    double s = 0.0;
+                    for (int i = -Rh; i <= Rh; ++i) s += wh[i + Rh] * b[((int64_t)t * Hh + reflect_index(h + i, Hh)) * Ww + w];
+                    a[((int64_t)t * Hh + h) * Ww + w] = s;
+                }
+        /* along w */
+        double ss = 0.0;
+        for (int64_t r = 0; r < (int64_t)T * Hh; ++r)
+            for (int w = 0; w < Ww; ++w) {
+                double s = 0.0;
+                for (int i = -Rw; i <= Rw; ++i) s += ww[i + Rw] * a[r * Ww + reflect_index(w + i, Ww)];
+                b[r * Ww + w] = s;
+                ss += s * s;
+            }
+        const double inv = 1.0 / sqrt(ss / (double)G);
+        const int nth = Hh / j->ph, ntw = Ww / j->pw, pts = j->pt * j->ph * j->pw;
+        for (int t = 0; t < T; ++t)
+            for (int h = 0; h < Hh; ++h)
+                for (int w = 0; w < Ww; ++w) {
+                    const int64_t tile = ((int64_t)(t / j->pt) * nth + h / j->ph) * ntw + w / j->pw;
+                    const int64_t row = tile * pts + ((t % j->pt) * j->ph + h % j->ph) * j->pw + w % j->pw;
+                    j->out[row * j->ld + c] = f32_to_bf16_bits((float)(b[((int64_t)t * Hh + h) * Ww + w] * inv));
+                }
+    }
+    free(a);
+    free(b);
+    return NULL;
+}
+
+void synth_smooth_field_bf16(uint64_t seed, uint64_t stream, int T, int Hh, int Ww, int C,
+                             double st, double sh, double sw, int pt, int ph, int pw,
+                             uint16_t* out, int64_t ld, int threads) {
+    if (threads < 1) threads = 1;
+    if (threads > 256) threads = 256;
+    if (threads > C) threads = C;
+    pthread_t tid[256];
+    field_job_t jobs[256];
+    const uint64_t key = stream_key(seed, stream);
+    for (int t = 0; t < threads; ++t) {
+        field_job_t* j = &jobs[t];
+        j->key = key; j->T = T; j->Hh = Hh; j->Ww = Ww; j->C = C;
+        j->pt = pt; j->ph = ph; j->pw = pw;
+        j->st = st; j->sh = sh; j->sw = sw;
+        j->c_begin = (int)((int64_t)C * t / threads);
+        j->c_end = (int)((int64_t)C * (t + 1) / threads);
+        j->out = out; j->ld = ld;
+    }
+    for (int t = 1; t < threads; ++t) pthread_create(&tid[t], NULL, run_field, &jobs[t]);
+    run_field(&jobs[0]);
+    for (int t = 1; t < threads; ++t) pthread_join(tid[t], NULL);
+}

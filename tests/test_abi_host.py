@@ -116,3 +116,17 @@ def test_layout_rejects_bad_shape():
     off = (ctypes.c_size_t * 7)()
     assert _native.load().vsa_workspace_layout(1, 64, 65, 0, off) == UNALIGNED
     assert _native.load().vsa_workspace_layout(1, 64, 64, 0, None) == NULLP
+
+
+def test_project_validation():
+    lib = _native.load()
+    o = [FAKE] * 4
+    assert lib.vsa_project_qkvg(FAKE, FAKE, 4, 96, 2, *o, None) == UNALIGNED   # hidden % 64
+    assert lib.vsa_project_qkvg(FAKE, FAKE, 4, 64, 3, *o, None) == UNALIGNED   # odd heads
+    assert lib.vsa_project_qkvg(FAKE, FAKE, 0, 64, 2, *o, None) == SHAPE
+    assert lib.vsa_project_qkvg(FAKE, FAKE, 4, 32, 2, *o, None) == SHAPE
+    assert lib.vsa_project_qkvg(None, FAKE, 4, 64, 2, *o, None) == NULLP
+    assert lib.vsa_project_qkvg(FAKE, FAKE, 4, 64, 2, FAKE, FAKE, None, FAKE, None) == NULLP
+    assert lib.vsa_project_qkvg(FAKE + 2, FAKE, 4, 64, 2, *o, None) == MISALIGNED
+    assert lib.vsa_project_qkvg(FAKE, FAKE, 4, 32768, 2, *o, None) == TOO_LARGE
+    assert lib.vsa_project_qkvg(FAKE, FAKE, 4, 64, 2048, *o, None) == TOO_LARGE
