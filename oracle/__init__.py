@@ -60,6 +60,15 @@ def _load():
         lib.vsa_oracle_fine.argtypes = [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _P, _I32, _P,
                                         _P, _I64, _P, _P, ctypes.c_int]
         lib.vsa_oracle_fine.restype = _I32
+        lib.vsa_oracle_select_coarse_valid.argtypes = [_P, _P, _P, _I32, _I64, _I64, _I64, _I64,
+                                                       _F64, _P, _P, _P, _P, _P, _P, _P,
+                                                       ctypes.c_int]
+        lib.vsa_oracle_select_coarse_valid.restype = _I32
+        lib.vsa_oracle_fine_valid.argtypes = [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I64, _I64,
+                                              _I64, _P, _I32, _P, _P, _I64, _P, _P, ctypes.c_int]
+        lib.vsa_oracle_fine_valid.restype = _I32
+        lib.vsa_oracle_pool_valid.argtypes = [_P, _I32, _I64, _I64, _I64, _P, ctypes.c_int]
+        lib.vsa_oracle_pool_valid.restype = None
         lib.vsa_oracle_bf16_from_f64.argtypes = [_F64]
         lib.vsa_oracle_bf16_from_f64.restype = ctypes.c_uint16
         lib.vsa_oracle_default_threads.argtypes = []
@@ -113,7 +122,10 @@ def row_scores(qbar: np.ndarray, kbar: np.ndarray, h: int, u: int) -> np.ndarray
 
 
 def select_coarse(q, k, v, text_len, video_len, audio_len, frac, want_scores=False,
-                  threads=None) -> dict:
+                  threads=None, video_valid=None) -> dict:
+    """Pooling, ranking, exact top-k and coarse branch for every (head, video
+    query tile).  video_valid: valid rows at the start of the video segment
+    (default all); tile means then cover valid rows only."""
     s = text_len + video_len + audio_len
     h = q.shape[1]
     q, k, v = (_check_tensor(x, s, h) for x in (q, k, v))
@@ -128,8 +140,9 @@ def select_coarse(q, k, v, text_len, video_len, audio_len, frac, want_scores=Fal
     coarse = np.empty((h, n_v, HEAD_DIM), np.float64)
     kth = np.empty((h, n_v), np.float64)
     scores = np.empty((h, n_v, n_v), np.float64) if want_scores else None
-    r = _load().vsa_oracle_select_coarse(
-        _ptr(q), _ptr(k), _ptr(v), h, text_len, video_len, audio_len, frac_as_passed(frac),
+    r = _load().vsa_oracle_select_coarse_valid(
+        _ptr(q), _ptr(k), _ptr(v), h, text_len, video_len, audio_len,
+        video_len if video_valid is None else video_valid, frac_as_passed(frac),
         _ptr(qbar), _ptr(kbar), _ptr(vbar), _ptr(sel), _ptr(coarse), _ptr(kth), _ptr(scores),
         threads or 0)
     if r < 0:
@@ -138,9 +151,12 @@ def select_coarse(q, k, v, text_len, video_len, audio_len, frac, want_scores=Fal
             "kth": kth, "scores": scores}
 
 
-def fine(q, k, v, gate, text_len, video_len, audio_len, sel, coarse, rows, threads=None):
-    """Rows `rows` of every head, on the given selection.  Returns
-    (bfloat16 bits [n_rows][H][128], float64 [n_rows][H][128])."""
+def fine(q, k, v, gate, text_len, video_len, audio_len, sel, coarse, rows, threads=None,
+         valid=None):
+    """Rows `rows` of every head, on the given selection.  valid = (text,
+    video, audio) valid rows at the start of each segment (default: all);
+    padding rows are never keys and output zeros.  Returns (bfloat16 bits
+    [n_rows][H][128], float64 [n_rows][H][128])."""
     s = text_len + video_len + audio_len
     h = q.shape[1]
     q, k, v, gate = (_check_tensor(x, s, h) for x in (q, k, v, gate))
@@ -153,9 +169,11 @@ def fine(q, k, v, gate, text_len, video_len, audio_len, sel, coarse, rows, threa
         np.zeros((h, 0, HEAD_DIM))
     out_b = np.empty((len(rows), h, HEAD_DIM), np.uint16)
     out_d = np.empty((len(rows), h, HEAD_DIM), np.float64)
-    r = _load().vsa_oracle_fine(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), h, text_len, video_len,
-                                audio_len, _ptr(sel), kk, _ptr(coarse), _ptr(rows), len(rows),
-                                _ptr(out_b), _ptr(out_d), threads or 0)
+    vt, vv, va = (text_len, video_len, audio_len) if valid is None else valid
+    r = _load().vsa_oracle_fine_valid(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), h, text_len,
+                                      video_len, audio_len, vt, vv, va, _ptr(sel), kk,
+                                      _ptr(coarse), _ptr(rows), len(rows), _ptr(out_b),
+                                      _ptr(out_d), threads or 0)
     if r < 0:
         raise ValueError("bad arguments")
     return out_b, out_d
@@ -192,3 +210,104 @@ def project_rows(x: np.ndarray, w: np.ndarray, rows) -> np.ndarray:
         wp = (w[p].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         out[p] = xr @ wp.T
     return out
+
+
+# ---------------------------------------------------------------------------
+# Attention preprocessing: Q/K RMSNorm and partial 3D RoPE
+# ---------------------------------------------------------------------------
+
+RMS_EPS = 1e-6
+ROPE_DIM = 96          # rotated dimensions per head (32 per grid axis)
+ROPE_BASE = 10000.0
+
+
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """float64 -> bfloat16 bits, one rounding to nearest with ties to even.
+    Values in the normal range are rounded in the float64 bit pattern (bit 45
+    of the fraction is bfloat16's last kept bit); the rest (bfloat16
+    subnormals, zero, non-finite) go through vsa_oracle_bf16_from_f64, which
+    the pins also compare against on random values."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    u = x.view(np.uint64)
+    lsb = (u >> np.uint64(45)) & np.uint64(1)
+    r = (u + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)
+    out = (r.view(np.float64).astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    a = np.abs(x)
+    odd = ~((a >= 2.0 ** -126) & (a < 2.0 ** 127))
+    if odd.any():
+        f = _load().vsa_oracle_bf16_from_f64
+        idx = np.flatnonzero(odd)
+        flat = out.reshape(-1)
+        for i in idx:
+            flat[i] = f(float(x.reshape(-1)[i]))
+    return out
+
+
+def _widen(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def video_positions(grid, tile, video_valid: int) -> np.ndarray:
+    """(t, h, w) latent-grid coordinates of video tokens 0 .. video_valid-1 in
+    tile-packed order: tiles of pt x ph x pw grid points in raster order over
+    the tile grid, points in raster order inside a tile."""
+    T_, Hh, Ww = grid
+    pt, ph, pw = tile
+    i = np.arange(video_valid, dtype=np.int64)
+    pts = pt * ph * pw
+    tile_id, off = i // pts, i % pts
+    nth, ntw = Hh // ph, Ww // pw
+    tt, th, tw = tile_id // (nth * ntw), (tile_id // ntw) % nth, tile_id % ntw
+    ot, oh, ow = off // (ph * pw), (off // pw) % ph, off % pw
+    return np.stack([tt * pt + ot, th * ph + oh, tw * pw + ow], axis=1)
+
+
+def rms_norm_rope(x: np.ndarray, gamma: np.ndarray, text_len, video_len, audio_len, valid,
+                  grid, tile) -> np.ndarray:
+    """Learned RMSNorm and partial 3D RoPE of Q or K, float64, as bfloat16 bits.
+
+    Page "UniServe: serving FastH3 at its fastest", section "Fused attention
+    preprocessing": the attention inputs go through a learned Q/K RMSNorm and
+    a partial RoPE before tile pooling; the SGLang Diffusion benchmark page
+    gives RoPE dimension 96 of the 128 and the exact-rounding order
+    (normalised values rounded before RoPE).  Readings where the pages are
+    silent: the norm is per head over its 128 dims,
+        y = x / sqrt(mean(x^2) + 1e-6) * gamma[h],  rounded to bfloat16;
+    RoPE rotates dims 0..95 of video tokens only (text and audio carry no
+    latent-grid position): axis a in (t, h, w) owns dims 32a .. 32a+31 as 16
+    interleaved pairs (2i, 2i+1) turned by pos_a * 10000^(-i/16),
+        (y0, y1) -> (y0 cos - y1 sin, y0 sin + y1 cos),
+    then rounded to bfloat16 again.  Padding rows (past each segment's valid
+    count) become zeros.
+
+    x: bfloat16 bits [S][H][128]; gamma: bfloat16 bits [H][128];
+    valid = (text, video, audio) valid rows; grid, tile as in
+    video_positions."""
+    S, H, Dh = x.shape
+    xf = _widen(x)
+    ms = (xf ** 2).mean(axis=2, keepdims=True)
+    y = xf / np.sqrt(ms + RMS_EPS) * _widen(gamma)[None, :, :]
+    yb = _widen(bf16_round(y))
+    vt, vv, va = valid
+    pos = video_positions(grid, tile, vv)
+    rows = np.arange(text_len, text_len + vv)
+    seg = yb[rows]                                    # [vv][H][128]
+    per_axis = ROPE_DIM // 3
+    half = per_axis // 2
+    inv = ROPE_BASE ** (-np.arange(half, dtype=np.float64) / half)
+    out = seg.copy()
+    for a in range(3):
+        ang = pos[:, a:a + 1].astype(np.float64) * inv[None, :]      # [vv][16]
+        c, s_ = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+        d0 = per_axis * a + 2 * np.arange(half)
+        x0, x1 = seg[:, :, d0], seg[:, :, d0 + 1]
+        out[:, :, d0] = x0 * c - x1 * s_
+        out[:, :, d0 + 1] = x0 * s_ + x1 * c
+    yb[rows] = out
+    res = bf16_round(yb)
+    pad = np.ones(S, bool)
+    pad[:vt] = False
+    pad[text_len:text_len + vv] = False
+    pad[text_len + video_len:text_len + video_len + va] = False
+    res[pad] = 0
+    return res

@@ -96,19 +96,23 @@ int32_t vsa_oracle_topk_count(int64_t n_v, double frac) {
 /* ------------------------------------------------------------------------ */
 
 /* "The FastH3 workload" (coarse branch over mean-pooled tiles) and "Fused
- * attention preprocessing" (the pooled statistics are FP32).  For head h and
- * tile u (tiles counted from token row0), the mean of the tile's 64 rows,
- * summed in row order in float64 and rounded once to float32.  out is
+ * attention preprocessing" (the pooled statistics are FP32, pooled over valid
+ * tokens).  For head h and tile u (tiles counted from token row0), the mean
+ * of the tile's valid rows -- the first `valid` rows from row0 are valid, so
+ * tile u has n = min(64, valid - 64u) of them -- summed in row order in
+ * float64, divided by n in float64 and rounded once to float32.  out is
  * [H][n_tiles][128]. */
-static void pool_one(const uint16_t* x, int32_t H, int64_t row0, int64_t n_tiles, int32_t h,
-                     int64_t u, float* out) {
+static void pool_one(const uint16_t* x, int32_t H, int64_t row0, int64_t n_tiles, int64_t valid,
+                     int32_t h, int64_t u, float* out) {
+    int64_t n = valid - u * T;
+    if (n > T) n = T;
     for (int d = 0; d < D; ++d) {
         double s = 0.0;
-        for (int r = 0; r < T; ++r) {
+        for (int64_t r = 0; r < n; ++r) {
             int64_t row = row0 + u * T + r;
             s += bf16_to_f64(x[(row * H + h) * D + d]);
         }
-        out[((int64_t)h * n_tiles + u) * D + d] = (float)(s / (double)T);
+        out[((int64_t)h * n_tiles + u) * D + d] = (float)(s / (double)n);
     }
 }
 
@@ -250,21 +254,29 @@ static void run_pool(void (*fn)(void*, int64_t, void*), void* ctx, int64_t n_ite
 typedef struct {
     const uint16_t* x;
     int32_t H;
-    int64_t row0, n_tiles;
+    int64_t row0, n_tiles, valid;
     float* out;
 } pool_ctx_t;
 
 static void pool_item(void* p, int64_t item, void* scratch) {
     (void)scratch;
     pool_ctx_t* c = (pool_ctx_t*)p;
-    pool_one(c->x, c->H, c->row0, c->n_tiles, (int32_t)(item / c->n_tiles), item % c->n_tiles, c->out);
+    pool_one(c->x, c->H, c->row0, c->n_tiles, c->valid, (int32_t)(item / c->n_tiles),
+             item % c->n_tiles, c->out);
 }
 
-/* Pooled FP32 means of n_tiles tiles starting at token row0, every head. */
+/* Pooled FP32 means of n_tiles tiles starting at token row0, every head, over
+ * the first `valid` rows (every tile must hold at least one). */
+void vsa_oracle_pool_valid(const uint16_t* x, int32_t H, int64_t row0, int64_t n_tiles,
+                           int64_t valid, float* out, int threads) {
+    pool_ctx_t c = {x, H, row0, n_tiles, valid, out};
+    run_pool(pool_item, &c, (int64_t)H * n_tiles, 0, threads);
+}
+
+/* Pooled FP32 means of n_tiles full tiles starting at token row0, every head. */
 void vsa_oracle_pool_threads(const uint16_t* x, int32_t H, int64_t row0, int64_t n_tiles, float* out,
                              int threads) {
-    pool_ctx_t c = {x, H, row0, n_tiles, out};
-    run_pool(pool_item, &c, (int64_t)H * n_tiles, 0, threads);
+    vsa_oracle_pool_valid(x, H, row0, n_tiles, n_tiles * T, out, threads);
 }
 
 void vsa_oracle_pool(const uint16_t* x, int32_t H, int64_t row0, int64_t n_tiles, float* out) {
@@ -306,23 +318,36 @@ static void select_item(void* p, int64_t item, void* scratch) {
  *   kth              : float64 [H][n_v]       (k-th largest score; may be NULL)
  *   scores           : float64 [H][n_v][n_v]  (all scores; may be NULL)
  * Returns k, or -1 on bad arguments. */
-int32_t vsa_oracle_select_coarse(const uint16_t* q, const uint16_t* kk, const uint16_t* v,
-                                 int32_t H, int64_t S_t, int64_t S_v, int64_t S_a, double frac,
-                                 float* qbar, float* kbar, float* vbar, int32_t* sel,
-                                 double* coarse, double* kth, double* scores, int threads) {
+/* As vsa_oracle_select_coarse, for a video segment whose first V_v of S_v
+ * rows are valid (S_v - 64 < V_v <= S_v: only the last tile may be partial):
+ * the pooled statistics average each tile's valid rows only. */
+int32_t vsa_oracle_select_coarse_valid(const uint16_t* q, const uint16_t* kk, const uint16_t* v,
+                                       int32_t H, int64_t S_t, int64_t S_v, int64_t S_a,
+                                       int64_t V_v, double frac, float* qbar, float* kbar,
+                                       float* vbar, int32_t* sel, double* coarse, double* kth,
+                                       double* scores, int threads) {
     (void)S_a;
     if (H < 1 || S_t % T || S_v % T || S_a % T || S_t < 0 || S_v < 0 || S_a < 0) return -1;
+    if (V_v > S_v || (S_v > 0 && V_v <= S_v - T)) return -1;
     int64_t n_v = S_v / T;
     int32_t k = vsa_oracle_topk_count(n_v, frac);
     if (k < 0) return -1;
     if (n_v == 0) return 0;
-    vsa_oracle_pool_threads(q, H, S_t, n_v, qbar, threads);
-    vsa_oracle_pool_threads(kk, H, S_t, n_v, kbar, threads);
-    vsa_oracle_pool_threads(v, H, S_t, n_v, vbar, threads);
+    vsa_oracle_pool_valid(q, H, S_t, n_v, V_v, qbar, threads);
+    vsa_oracle_pool_valid(kk, H, S_t, n_v, V_v, kbar, threads);
+    vsa_oracle_pool_valid(v, H, S_t, n_v, V_v, vbar, threads);
     select_ctx_t c = {qbar, kbar, vbar, n_v, k, sel, coarse, kth, scores};
     size_t scratch = sizeof(double) * (size_t)n_v + sizeof(scored_t) * (size_t)n_v;
     run_pool(select_item, &c, (int64_t)H * n_v, scratch, threads);
     return k;
+}
+
+int32_t vsa_oracle_select_coarse(const uint16_t* q, const uint16_t* kk, const uint16_t* v,
+                                 int32_t H, int64_t S_t, int64_t S_v, int64_t S_a, double frac,
+                                 float* qbar, float* kbar, float* vbar, int32_t* sel,
+                                 double* coarse, double* kth, double* scores, int threads) {
+    return vsa_oracle_select_coarse_valid(q, kk, v, H, S_t, S_v, S_a, S_v, frac, qbar, kbar, vbar,
+                                          sel, coarse, kth, scores, threads);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -333,6 +358,7 @@ typedef struct {
     const uint16_t *q, *k, *v, *g;
     int32_t H;
     int64_t S_t, S_v, S_a;
+    int64_t V_t, V_v, V_a; /* valid rows at the start of each segment */
     const int32_t* sel; /* [H][n_v][kk] */
     int32_t kk;
     const double* coarse; /* [H][n_v][128] */
@@ -349,7 +375,17 @@ typedef struct {
  * keys, with logits q.k / sqrt(128).
  * "Fused output combination": a video row adds the gated coarse output of its
  * tile; the gate is sigmoid(G) per channel.  Text and audio rows have no
- * coarse term.  The result is rounded once to bfloat16. */
+ * coarse term.  The result is rounded once to bfloat16.
+ * "Fused attention preprocessing" (padding handled inside the kernel, never
+ * an input to later computation).  Reading: each segment's first V rows are
+ * its tokens and the rest padding; padding rows are never keys, and a
+ * padding query row outputs zeros. */
+static int is_valid_row(const fine_ctx_t* c, int64_t j) {
+    if (j < c->S_t) return j < c->V_t;
+    if (j < c->S_t + c->S_v) return j - c->S_t < c->V_v;
+    return j - c->S_t - c->S_v < c->V_a;
+}
+
 static void fine_item(void* p, int64_t item, void* scratch) {
     fine_ctx_t* c = (fine_ctx_t*)p;
     const int32_t H = c->H;
@@ -364,15 +400,29 @@ static void fine_item(void* p, int64_t item, void* scratch) {
 
     int64_t* keys = (int64_t*)scratch;
     double* logit = (double*)(keys + S);
+    int64_t base = (ri * H + h) * D;
+    if (!is_valid_row(c, i)) {
+        for (int d = 0; d < D; ++d) {
+            if (c->out_f64) c->out_f64[base + d] = 0.0;
+            c->out_bf16[base + d] = 0;
+        }
+        return;
+    }
     int64_t nk = 0;
     if (!is_video) {
-        for (int64_t j = 0; j < S; ++j) keys[nk++] = j;
+        for (int64_t j = 0; j < S; ++j)
+            if (is_valid_row(c, j)) keys[nk++] = j;
     } else {
-        for (int64_t j = 0; j < c->S_t; ++j) keys[nk++] = j;
+        for (int64_t j = 0; j < c->S_t; ++j)
+            if (is_valid_row(c, j)) keys[nk++] = j;
         const int32_t* srow = c->sel + ((int64_t)h * n_v + u) * c->kk;
         for (int32_t t = 0; t < c->kk; ++t)
-            for (int r = 0; r < T; ++r) keys[nk++] = c->S_t + (int64_t)srow[t] * T + r;
-        for (int64_t j = c->S_t + c->S_v; j < S; ++j) keys[nk++] = j;
+            for (int r = 0; r < T; ++r) {
+                const int64_t j = c->S_t + (int64_t)srow[t] * T + r;
+                if (is_valid_row(c, j)) keys[nk++] = j;
+            }
+        for (int64_t j = c->S_t + c->S_v; j < S; ++j)
+            if (is_valid_row(c, j)) keys[nk++] = j;
     }
 
     double qi[D];
@@ -393,7 +443,6 @@ static void fine_item(void* p, int64_t item, void* scratch) {
         const uint16_t* vj = c->v + (keys[t] * H + h) * D;
         for (int d = 0; d < D; ++d) o[d] += e * bf16_to_f64(vj[d]);
     }
-    int64_t base = (ri * H + h) * D;
     for (int d = 0; d < D; ++d) {
         double y = o[d] / den;
         if (is_video) {
@@ -411,11 +460,13 @@ static void fine_item(void* p, int64_t item, void* scratch) {
  * `coarse` ([H][n_v][128], float64).  Taking the selection as an argument
  * lets a test evaluate the fine branch on exactly the index sets another
  * implementation chose.  Returns 0, or -1 on bad arguments. */
-int32_t vsa_oracle_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
-                        int32_t H, int64_t S_t, int64_t S_v, int64_t S_a, const int32_t* sel,
-                        int32_t kk, const double* coarse, const int64_t* rows, int64_t n_rows,
-                        uint16_t* out_bf16, double* out_f64, int threads) {
+int32_t vsa_oracle_fine_valid(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                              const uint16_t* g, int32_t H, int64_t S_t, int64_t S_v, int64_t S_a,
+                              int64_t V_t, int64_t V_v, int64_t V_a, const int32_t* sel,
+                              int32_t kk, const double* coarse, const int64_t* rows,
+                              int64_t n_rows, uint16_t* out_bf16, double* out_f64, int threads) {
     if (H < 1 || S_t % T || S_v % T || S_a % T || S_t < 0 || S_v < 0 || S_a < 0) return -1;
+    if (V_t < 0 || V_t > S_t || V_v < 0 || V_v > S_v || V_a < 0 || V_a > S_a) return -1;
     int64_t S = S_t + S_v + S_a;
     for (int64_t r = 0; r < n_rows; ++r)
         if (rows[r] < 0 || rows[r] >= S) return -1;
@@ -425,10 +476,19 @@ int32_t vsa_oracle_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v,
         for (int64_t e = 0; e < (int64_t)H * n_v * kk; ++e)
             if (sel[e] < 0 || sel[e] >= n_v) return -1;
     }
-    fine_ctx_t c = {q, k, v, g, H, S_t, S_v, S_a, sel, kk, coarse, rows, n_rows, out_bf16, out_f64};
+    fine_ctx_t c = {q, k, v, g, H, S_t, S_v, S_a, V_t, V_v, V_a, sel, kk, coarse, rows, n_rows,
+                    out_bf16, out_f64};
     size_t scratch = (sizeof(int64_t) + sizeof(double)) * (size_t)S;
     run_pool(fine_item, &c, n_rows * H, scratch, threads);
     return 0;
+}
+
+int32_t vsa_oracle_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* g,
+                        int32_t H, int64_t S_t, int64_t S_v, int64_t S_a, const int32_t* sel,
+                        int32_t kk, const double* coarse, const int64_t* rows, int64_t n_rows,
+                        uint16_t* out_bf16, double* out_f64, int threads) {
+    return vsa_oracle_fine_valid(q, k, v, g, H, S_t, S_v, S_a, S_t, S_v, S_a, sel, kk, coarse,
+                                 rows, n_rows, out_bf16, out_f64, threads);
 }
 
 /* Threads a call with threads <= 0 would use. */

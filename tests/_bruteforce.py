@@ -16,11 +16,19 @@ def widen(bits: np.ndarray) -> np.ndarray:
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def vsa_dense_masked(q, k, v, g, s_t, s_v, s_a, kk):
-    """Returns (out float64 [S,H,128], sel int [H,n_v,kk], coarse [H,n_v,128], mask [H,S,S])."""
+def vsa_dense_masked(q, k, v, g, s_t, s_v, s_a, kk, valid=None):
+    """Returns (out float64 [S,H,128], sel int [H,n_v,kk], coarse [H,n_v,128], mask [H,S,S]).
+    valid = (text, video, audio) rows at the start of each segment that are
+    tokens (default all); the others are padding: never keys, zero outputs,
+    and left out of the tile means."""
     Q, K, V, G = (widen(x) for x in (q, k, v, g))
     S, H, _ = Q.shape
     n_v = s_v // T
+    vt, vv, va = (s_t, s_v, s_a) if valid is None else valid
+    tok = np.zeros(S, dtype=bool)
+    tok[:vt] = True
+    tok[s_t:s_t + vv] = True
+    tok[s_t + s_v:s_t + s_v + va] = True
     alpha = 1.0 / np.sqrt(D)
     out = np.zeros((S, H, D))
     sel = np.zeros((H, n_v, kk), dtype=np.int64)
@@ -29,8 +37,10 @@ def vsa_dense_masked(q, k, v, g, s_t, s_v, s_a, kk):
     for h in range(H):
         if n_v:
             # FP32 pooled statistics of the video tiles
-            pooled = [X[s_t:s_t + s_v, h, :].reshape(n_v, T, D).mean(axis=1).astype(np.float32)
-                      .astype(np.float64) for X in (Q, K, V)]
+            vid_tok = tok[s_t:s_t + s_v].reshape(n_v, T, 1)
+            pooled = [((X[s_t:s_t + s_v, h, :].reshape(n_v, T, D) * vid_tok).sum(axis=1)
+                       / vid_tok.sum(axis=1)).astype(np.float32).astype(np.float64)
+                      for X in (Q, K, V)]
             qb, kb, vb = pooled
             scores = qb @ kb.T                      # [n_v (query tile), n_v (key tile)]
             for u in range(n_v):
@@ -51,6 +61,7 @@ def vsa_dense_masked(q, k, v, g, s_t, s_v, s_a, kk):
                 mask[i] = ~key_is_video | np.isin(tile_of, list(allowed_video_tiles))
             else:
                 mask[i] = True
+        mask &= tok[None, :]
         masks[h] = mask
         logits = alpha * (Q[:, h, :] @ K[:, h, :].T)
         logits = np.where(mask, logits, -np.inf)
@@ -60,5 +71,6 @@ def vsa_dense_masked(q, k, v, g, s_t, s_v, s_a, kk):
             vid = slice(s_t, s_t + s_v)
             c_rows = np.repeat(coarse[h], T, axis=0)  # broadcast each tile's output to its 64 rows
             o[vid] = o[vid] + (1.0 / (1.0 + np.exp(-G[vid, h, :]))) * c_rows
+        o[~tok] = 0.0
         out[:, h, :] = o
     return out, sel, coarse, masks
