@@ -179,3 +179,33 @@ def project_qkvg(x, w, num_heads, stream=None):
             for _ in range(4)]
     vsa_project_qkvg(x, w, num_heads, *outs, stream=stream)
     return tuple(outs)
+
+
+def vsa_forward_padded(q, k, v, gate, text_len, video_len, audio_len, valid, topk_frac, out,
+                       selected_tiles, workspace, gamma_q=None, gamma_k=None, grid=None,
+                       tile=(2, 8, 4), q_out=None, stream=None):
+    """vsa_forward on padded segments (valid = (text, video, audio) token
+    rows), optionally with Q/K RMSNorm + partial 3D RoPE fused into stage 1
+    (gamma_q, gamma_k bf16 [H][128]; grid = latent (T, H, W) of the video
+    tokens; q_out receives the preprocessed q)."""
+    torch = _torch()
+    shp = _shape_args(q, text_len, video_len, audio_len)
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
+        _tensor(t, n, torch.bfloat16, shp)
+    _tensor(gate, "gate", torch.bfloat16, shp)
+    if selected_tiles is not None:
+        _tensor(selected_tiles, "selected_tiles", torch.int32)
+    g6 = None
+    if gamma_q is not None or gamma_k is not None:
+        _tensor(gamma_q, "gamma_q", torch.bfloat16, (shp[1], HEAD_DIM))
+        _tensor(gamma_k, "gamma_k", torch.bfloat16, (shp[1], HEAD_DIM))
+        _tensor(q_out, "q_out", torch.bfloat16, shp)
+        g6 = (ctypes.c_int32 * 6)(*grid, *tile)
+    _check(load().vsa_forward_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(gamma_q),
+                                     _ptr(gamma_k), g6, shp[1], text_len, video_len, audio_len,
+                                     valid[0], valid[1], valid[2], topk_frac, _ptr(q_out),
+                                     _ptr(out), _ptr(selected_tiles),
+                                     _ptr(workspace) if workspace is not None else None,
+                                     workspace.numel() if workspace is not None else 0,
+                                     _stream(stream)),
+           "vsa_forward_padded")

@@ -25,6 +25,8 @@ SIGNATURES = {
     "vsa_select_coarse": (ctypes.c_int, [_I32, _I64, _I64, _I64, _F32, _P, _P, _SZ, _P]),
     "vsa_fine_attention": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _F32, _P, _P, _P, _SZ, _P]),
     "vsa_project_qkvg": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P]),
+    "vsa_forward_padded": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64,
+                                          _I64, _I64, _I64, _F32, _P, _P, _P, _P, _SZ, _P]),
 }
 
 _lib = None

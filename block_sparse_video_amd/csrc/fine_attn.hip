@@ -56,7 +56,8 @@ struct FineArgs {
     const float* coarse;
     uint16_t* out;
     int H, n_t, n_v, n_a, N, kk;
-    float scale_log2;  // log2(e) / sqrt(128)
+    int last_valid[3];  // token rows in the last text / video / audio tile (64 when full)
+    float scale_log2;   // log2(e) / sqrt(128)
 };
 
 // blockIdx -> (head, query tile).  All video units come first, head-major,
@@ -83,6 +84,28 @@ __device__ __forceinline__ void unit_of(int b, int H, int n_t, int n_v, int n_a,
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Token (non-padding) rows of global tile t: 64 except in a segment's last
+// tile when the segment is padded.  Padding rows are never keys and output
+// zeros (page "UniServe: serving FastH3 at its fastest", section "Fused
+// attention preprocessing": padding never becomes an input of later steps).
+__device__ __forceinline__ int tile_rows(const FineArgs& a, int t) {
+    if (t == a.n_t - 1) return a.last_valid[0];
+    if (t == a.n_t + a.n_v - 1) return a.last_valid[1];
+    if (t == a.N - 1) return a.last_valid[2];
+    return kT;
+}
+
+// Drop the keys at or past `nvh` (keys of a half-tile, in packed order) from
+// one S^T block: lane l, element e holds key kappa(8(e/4) + 4(l/32) + e%4).
+__device__ __forceinline__ void mask_keys(f32x16& s, int nvh, int g) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const int r = 8 * (e >> 2) + 4 * g + (e & 3);
+        const int key = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+        if (key >= nvh) s[e] = -__builtin_inff();
+    }
 }
 
 __device__ __forceinline__ float sigmoidf(float g) {
@@ -250,6 +273,19 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         for (int s8 = 0; s8 < 8; ++s8) qf[qb][s8] = *(const bf16x8*)(qp + 16 * s8);
     }
     wait_vmcnt(0);  // Q is resident before the ring starts counting loads
+    // padding query rows (past the tile's token rows) attend with zeros and
+    // are written as zeros
+    const int nq = tile_rows(a, j);
+    if (nq < kT) {
+        bf16x8 z8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) z8[i] = (__bf16)0.0f;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+            if (32 * qb + l32 >= nq)
+#pragma unroll
+                for (int s8 = 0; s8 < 8; ++s8) qf[qb][s8] = z8;
+    }
 
     const int t0 = tile_at(0), t1 = tile_at(1);
 
@@ -316,6 +352,13 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         for (int i = 0; i < 8; ++i) vop[i] = zero8;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) pprev[qb][0] = pprev[qb][1] = zero8;
+        {
+            const int nv0 = tile_rows(a, t0);  // S^T(0) is half 0 of the first tile
+            if (nv0 < 32) {
+                mask_keys(sc[0], nv0, g);
+                mask_keys(sc[1], nv0, g);
+            }
+        }
         if (pass == 0) {
             m_ref[0] = column_max(sc[0], c2);
             m_ref[1] = column_max(sc[1], c2);
@@ -327,6 +370,7 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         int xm3 = 0;
         for (int t = 0; t < n_tiles; ++t) {
             const int nn = tile_at(t + 2);
+            const int rows_cur = tile_rows(a, cur);  // token rows of the tile in use
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp) {
                 // step x = 2t + pp
@@ -338,6 +382,14 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
                 fetch_k(kslot(k_wr), nn, pp);
                 f32x16 n0 = zero16, n1 = zero16;
                 bf16x8 pc[2][2];
+                {
+                    // keys of half pp of the current tile that are tokens
+                    const int nvh = rows_cur - 32 * pp;
+                    if (nvh < 32) {
+                        mask_keys(sc[0], nvh, g);
+                        mask_keys(sc[1], nvh, g);
+                    }
+                }
 #pragma unroll
                 for (int s8 = 0; s8 < 8; ++s8) {
                     n0 = mfma32(kop[s8], qf[0][s8], n0);
@@ -413,7 +465,10 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         const float4 x1 = *(const float4*)(ost + row * kD + 4 * ((2 * c + 1) ^ (row & 15)));
         f32x8 y = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         const int64_t grow = (int64_t)j * kT + row;
-        if (video) {
+        if (row >= nq) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+        } else if (video) {
             const uint4 gw = *(const uint4*)(a.gate + grow * rs + (int64_t)h * kD + 8 * c);
             const float4 c0 = *(const float4*)(cp + 8 * c);
             const float4 c1 = *(const float4*)(cp + 8 * c + 4);
@@ -448,6 +503,9 @@ hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate, const 
     a.n_a = s.n_a;
     a.N = s.N;
     a.kk = s.k;
+    a.last_valid[0] = s.n_t ? (int)(s.V_t - 64 * (int64_t)(s.n_t - 1)) : kT;
+    a.last_valid[1] = s.n_v ? (int)(s.V_v - 64 * (int64_t)(s.n_v - 1)) : kT;
+    a.last_valid[2] = s.n_a ? (int)(s.V_a - 64 * (int64_t)(s.n_a - 1)) : kT;
     a.scale_log2 = (float)(1.4426950408889634 / 11.313708498984761);
     const int64_t units = (int64_t)s.H * s.N;
     hipLaunchKernelGGL(fine_attn_kernel, dim3((unsigned)units), dim3(kThreads), 0, stream, a);

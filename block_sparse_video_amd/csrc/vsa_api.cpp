@@ -37,6 +37,9 @@ vsa_status make_shape(int32_t H, int64_t S_t, int64_t S_v, int64_t S_a, Shape* s
     s->n_a = (int32_t)(S_a / VSA_TILE);
     s->N = s->n_t + s->n_v + s->n_a;
     s->k = 0;
+    s->V_t = S_t;
+    s->V_v = S_v;
+    s->V_a = S_a;
     return VSA_OK;
 }
 
@@ -238,6 +241,70 @@ vsa_status vsa_forward(const void* q, const void* k, const void* v, const void* 
     if (e == hipSuccess)
         e = vsa::launch_fine_attention((const uint16_t*)q, (const uint16_t*)gate,
                                        selected_tiles, (uint16_t*)out, s, ws, L, strm);
+    return from_hip(e);
+}
+
+vsa_status vsa_forward_padded(const void* q, const void* k, const void* v, const void* gate,
+                              const void* gamma_q, const void* gamma_k, const int32_t grid[6],
+                              int32_t num_heads, int64_t text_len, int64_t video_len,
+                              int64_t audio_len, int64_t text_valid, int64_t video_valid,
+                              int64_t audio_valid, float topk_frac, void* q_out, void* out,
+                              int32_t* selected_tiles, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+    if (!q || !k || !v || !out) return VSA_ERR_NULL_POINTER;
+    if (video_len != 0 && (!gate || !selected_tiles)) return VSA_ERR_NULL_POINTER;
+    const bool prep = gamma_q || gamma_k;
+    if (prep && (!gamma_q || !gamma_k || !q_out || !grid)) return VSA_ERR_NULL_POINTER;
+    Shape s;
+    vsa_status st = make_shape(num_heads, text_len, video_len, audio_len, &s);
+    if (st != VSA_OK) return st;
+    // each segment: its first `valid` rows are tokens, and only its last tile
+    // may hold padding
+    const int64_t lens[3] = {text_len, video_len, audio_len};
+    const int64_t vals[3] = {text_valid, video_valid, audio_valid};
+    for (int i = 0; i < 3; ++i) {
+        if (lens[i] == 0 ? vals[i] != 0 : (vals[i] > lens[i] || vals[i] <= lens[i] - VSA_TILE))
+            return VSA_ERR_BAD_SHAPE;
+    }
+    s.V_t = text_valid;
+    s.V_v = video_valid;
+    s.V_a = audio_valid;
+    vsa::Prep pp{};
+    if (prep) {
+        for (int i = 0; i < 6; ++i)
+            if (grid[i] < 1) return VSA_ERR_BAD_SHAPE;
+        for (int i = 0; i < 3; ++i)
+            if (grid[i] % grid[3 + i]) return VSA_ERR_BAD_SHAPE;
+        if ((int64_t)grid[0] * grid[1] * grid[2] != video_valid) return VSA_ERR_BAD_SHAPE;
+        pp.gamma_q = (const uint16_t*)gamma_q;
+        pp.gamma_k = (const uint16_t*)gamma_k;
+        for (int i = 0; i < 3; ++i) {
+            pp.grid[i] = grid[i];
+            pp.tile[i] = grid[3 + i];
+        }
+    }
+    if ((st = check_topk(topk_frac, &s)) != VSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        (gate && !aligned(gate, 16)) || (selected_tiles && !aligned(selected_tiles, 16)) ||
+        (prep && (!aligned(q_out, 16) || !aligned(gamma_q, 16) || !aligned(gamma_k, 16))))
+        return VSA_ERR_MISALIGNED;
+    const Layout L = vsa::make_layout(s);
+    if (workspace) {
+        if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
+    }
+    if ((st = check_device()) != VSA_OK) return st;
+    if (!workspace) {
+        if ((st = owned_workspace(L.total, &workspace)) != VSA_OK) return st;
+    }
+    hipStream_t strm = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    hipError_t e = vsa::launch_pool_pack((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                         s, ws, L, strm, prep ? &pp : nullptr, (uint16_t*)q_out);
+    if (e == hipSuccess && s.n_v > 0) e = vsa::launch_select_coarse(s, selected_tiles, ws, L, strm);
+    if (e == hipSuccess)
+        e = vsa::launch_fine_attention(prep ? (const uint16_t*)q_out : (const uint16_t*)q,
+                                       (const uint16_t*)gate, selected_tiles, (uint16_t*)out, s, ws,
+                                       L, strm);
     return from_hip(e);
 }
 

@@ -17,6 +17,27 @@ struct Shape {
     int64_t S_t, S_v, S_a, S;
     int32_t n_t, n_v, n_a, N;  // tile counts
     int32_t k;                 // selected tiles per video query tile
+    // valid (token) rows at the start of each segment; the rest of the
+    // segment's last tile is padding (S_x - 64 < V_x <= S_x when S_x > 0)
+    int64_t V_t, V_v, V_a;
+};
+
+// Valid rows of global tile j (64 for every tile but a segment's last).
+__host__ __device__ inline int tile_valid_rows(const Shape& s, int j) {
+    int64_t v;
+    if (j < s.n_t) v = s.V_t - 64 * (int64_t)j;
+    else if (j < s.n_t + s.n_v) v = s.V_v - 64 * (int64_t)(j - s.n_t);
+    else v = s.V_a - 64 * (int64_t)(j - s.n_t - s.n_v);
+    return v >= 64 ? 64 : (v > 0 ? (int)v : 0);
+}
+
+// Attention preprocessing (learned Q/K RMSNorm, partial 3D RoPE of video
+// tokens at their latent-grid positions).  gamma_q == nullptr: none.
+struct Prep {
+    const uint16_t* gamma_q;  // bf16 [H][128]
+    const uint16_t* gamma_k;  // bf16 [H][128]
+    int32_t grid[3];          // latent grid T x H x W of the valid video tokens
+    int32_t tile[3];          // tile-packing shape
 };
 
 // Workspace regions (byte offsets from the workspace base).
@@ -48,7 +69,8 @@ inline Layout make_layout(const Shape& s) {
 
 // ---- launchers (each enqueues on `stream`, returns the launch status) ----
 hipError_t launch_pool_pack(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                            const Shape& s, uint8_t* ws, const Layout& L, hipStream_t stream);
+                            const Shape& s, uint8_t* ws, const Layout& L, hipStream_t stream,
+                            const Prep* prep = nullptr, uint16_t* q_out = nullptr);
 hipError_t launch_select_coarse(const Shape& s, int32_t* sel, uint8_t* ws, const Layout& L,
                                 hipStream_t stream);
 hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate,

@@ -145,6 +145,40 @@ vsa_status vsa_fine_attention(const void* q, const void* gate, int32_t num_heads
                               float topk_frac, const int32_t* selected_tiles, void* out,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* The forward pass on padded segments, optionally with the attention
+ * preprocessing fused into stage 1 (page "UniServe: serving FastH3 at its
+ * fastest", section "Fused attention preprocessing": learned Q/K RMSNorm,
+ * partial RoPE and tile pooling over valid tokens in one pass, padding
+ * handled inside the kernel).
+ *   text_valid, video_valid, audio_valid: the first `valid` rows of each
+ *     segment are tokens, the rest padding; only a segment's last tile may be
+ *     padded (len - 64 < valid <= len; valid == 0 when len == 0).  Padding
+ *     rows are never keys, are left out of the tile means, and output zeros.
+ *   gamma_q, gamma_k: bf16 [H][128] learned RMSNorm weights, or both NULL for
+ *     no preprocessing (q and k are then used as given; q_out and grid are
+ *     ignored).  With them, every token row of q and k becomes
+ *       y = bf16(x / sqrt(mean over the head's 128 dims of x^2 + 1e-6) * gamma),
+ *     and video tokens then rotate dims 0..95 -- axis a of (t, h, w) owns dims
+ *     32a .. 32a+31 as 16 interleaved pairs (2i, 2i+1) -- by the angle
+ *     pos_a * 10000^(-i/16), rounded to bf16 again (the RoPE dimension 96 and
+ *     the rounding order follow the SGLang Diffusion benchmark page, section
+ *     "How SubBlock Sparse Attention Works" and its kernel table).  Text and
+ *     audio tokens are not rotated.
+ *   grid: {T, H, W, pt, ph, pw}: the valid video tokens are the T x H x W
+ *     latent grid points in tile-packed order (tiles of pt x ph x pw points
+ *     in raster order, raster order inside a tile); T*H*W == video_valid.
+ *   q_out: bf16 [S][H][128], receives the preprocessed q (padding rows zero);
+ *     the attention reads it.  The preprocessed k lives only in the
+ *     workspace (packed).
+ * Everything else as vsa_forward; workspace may be NULL. */
+vsa_status vsa_forward_padded(const void* q, const void* k, const void* v, const void* gate,
+                              const void* gamma_q, const void* gamma_k, const int32_t grid[6],
+                              int32_t num_heads, int64_t text_len, int64_t video_len,
+                              int64_t audio_len, int64_t text_valid, int64_t video_valid,
+                              int64_t audio_valid, float topk_frac, void* q_out, void* out,
+                              int32_t* selected_tiles, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* The Q, K, V and gate projections that produce this path's inputs (page
  * "UniServe: serving FastH3 at its fastest", section "The FastH3 workload":
  * hidden size 5,376, 56 heads of 128, so each projection maps 5,376 channels

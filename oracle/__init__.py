@@ -263,7 +263,7 @@ def video_positions(grid, tile, video_valid: int) -> np.ndarray:
 
 
 def rms_norm_rope(x: np.ndarray, gamma: np.ndarray, text_len, video_len, audio_len, valid,
-                  grid, tile) -> np.ndarray:
+                  grid, tile, rows=None) -> np.ndarray:
     """Learned RMSNorm and partial 3D RoPE of Q or K, float64, as bfloat16 bits.
 
     Page "UniServe: serving FastH3 at its fastest", section "Fused attention
@@ -282,32 +282,33 @@ def rms_norm_rope(x: np.ndarray, gamma: np.ndarray, text_len, video_len, audio_l
 
     x: bfloat16 bits [S][H][128]; gamma: bfloat16 bits [H][128];
     valid = (text, video, audio) valid rows; grid, tile as in
-    video_positions."""
+    video_positions; rows: token rows to return (default all).  Returns
+    bfloat16 bits [len(rows)][H][128]."""
     S, H, Dh = x.shape
-    xf = _widen(x)
+    rows = np.arange(S, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    xf = _widen(x[rows])
     ms = (xf ** 2).mean(axis=2, keepdims=True)
-    y = xf / np.sqrt(ms + RMS_EPS) * _widen(gamma)[None, :, :]
-    yb = _widen(bf16_round(y))
+    yb = _widen(bf16_round(xf / np.sqrt(ms + RMS_EPS) * _widen(gamma)[None, :, :]))
     vt, vv, va = valid
-    pos = video_positions(grid, tile, vv)
-    rows = np.arange(text_len, text_len + vv)
-    seg = yb[rows]                                    # [vv][H][128]
-    per_axis = ROPE_DIM // 3
-    half = per_axis // 2
-    inv = ROPE_BASE ** (-np.arange(half, dtype=np.float64) / half)
-    out = seg.copy()
-    for a in range(3):
-        ang = pos[:, a:a + 1].astype(np.float64) * inv[None, :]      # [vv][16]
-        c, s_ = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
-        d0 = per_axis * a + 2 * np.arange(half)
-        x0, x1 = seg[:, :, d0], seg[:, :, d0 + 1]
-        out[:, :, d0] = x0 * c - x1 * s_
-        out[:, :, d0 + 1] = x0 * s_ + x1 * c
-    yb[rows] = out
+    is_video = (rows >= text_len) & (rows < text_len + vv)
+    vid = np.flatnonzero(is_video)
+    if len(vid):
+        pos_all = video_positions(grid, tile, vv)
+        pos = pos_all[rows[vid] - text_len]
+        seg = yb[vid]
+        per_axis = ROPE_DIM // 3
+        half = per_axis // 2
+        inv = ROPE_BASE ** (-np.arange(half, dtype=np.float64) / half)
+        out = seg.copy()
+        for a in range(3):
+            ang = pos[:, a:a + 1].astype(np.float64) * inv[None, :]      # [n][16]
+            c, s_ = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+            d0 = per_axis * a + 2 * np.arange(half)
+            x0, x1 = seg[:, :, d0], seg[:, :, d0 + 1]
+            out[:, :, d0] = x0 * c - x1 * s_
+            out[:, :, d0 + 1] = x0 * s_ + x1 * c
+        yb[vid] = out
     res = bf16_round(yb)
-    pad = np.ones(S, bool)
-    pad[:vt] = False
-    pad[text_len:text_len + vv] = False
-    pad[text_len + video_len:text_len + video_len + va] = False
-    res[pad] = 0
+    tok = (rows < vt) | is_video | ((rows >= text_len + video_len) & (rows < text_len + video_len + va))
+    res[~tok] = 0
     return res

@@ -95,6 +95,22 @@ def read_workspace(ws: torch.Tensor, h, s_t, s_v, s_a) -> dict:
             "coarse": view(lay["coarse"], np.float32, (h, n_v, D))}
 
 
+def unpack_k(ws: torch.Tensor, h, s_t, s_v, s_a) -> np.ndarray:
+    """The (preprocessed) K the attention stage reads, from the workspace's
+    packed tiles, as bf16 bits [S][H][128].  Packed order per (head, tile):
+    [half 2][s 8][lane 64][8]: lane (r = lane % 32, g = lane / 32) holds
+    K[key 32*half + kappa(r)][dims 16s + 8g .. +7], kappa swapping bits 2, 3."""
+    lay = bsv.vsa_workspace_layout(h, s_t, s_v, s_a)
+    n = (s_t + s_v + s_a) // T
+    raw = ws[lay["kpack"]: lay["kpack"] + h * n * T * D * 2].cpu().numpy().view(np.uint16)
+    pk = raw.reshape(h, n, 2, 8, 2, 32, 8)            # [h][tile][half][s][g][r][e]
+    r = np.arange(32)
+    kap = (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1)
+    out = np.empty((h, n, 2, 32, 8, 2, 8), np.uint16)  # [h][tile][half][key][s][g][e]
+    out[:, :, :, kap] = pk.transpose(0, 1, 2, 5, 3, 4, 6)
+    return out.reshape(h, n * T, D).transpose(1, 0, 2).copy()
+
+
 def sample_rows(s_t, s_v, s_a, n_video_tiles=6, seed=0, per_tile=(0, 21, 42, 63)):
     """Seeded sample of query rows: first and last text and audio tiles, and
     a few video tiles (first, last and random ones), a few rows per tile."""
