@@ -186,6 +186,47 @@ def full_layer(bsv, torch, np, frac, steps, warmup, threads):
             "steps": steps}
 
 
+def pages_request(bsv, torch, np, frac, steps, warmup, threads):
+    """The 10 s request as the pages describe it: 1,000 text, 72,576 video
+    (18 x 48 x 84 latent grid) and 810 audio tokens, padded to whole tiles
+    (1,024 / 72,576 / 832 rows), 56 heads, with the learned Q/K RMSNorm and
+    partial 3D RoPE fused into stage 1 (vsa_forward_padded).  Inputs iid
+    N(0, 2^2) (raw projections before the norm), gammas N(1, 0.2^2)."""
+    import synth
+    h, s_t, s_v, s_a = 56, 1024, 72576, 832
+    valid = (1000, 72576, 810)
+    x = synth.vsa_inputs(7, h, s_t, s_v, s_a, std=2.0, threads=threads)
+    xd = {n: to_dev(a, np, torch) for n, a in x.items()}
+    del x
+    gq = to_dev(synth.normal_bf16(7, 20, (h, D), mean=1.0, std=0.2), np, torch)
+    gk = to_dev(synth.normal_bf16(7, 21, (h, D), mean=1.0, std=0.2), np, torch)
+    out, sel, ws = bsv.alloc_outputs(h, s_t, s_v, s_a, frac)
+    q_out = torch.empty_like(xd["q"])
+
+    def step():
+        bsv.vsa_forward_padded(xd["q"], xd["k"], xd["v"], xd["gate"], s_t, s_v, s_a, valid, frac,
+                               out, sel, ws, gamma_q=gq, gamma_k=gk, grid=(18, 48, 84),
+                               tile=(2, 8, 4), q_out=q_out)
+
+    for _ in range(warmup):
+        step()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    kk = bsv.vsa_topk_count(s_v, frac)
+    flops = tile_pairs(h, s_t, s_v, s_a, kk) * FLOP_PER_PAIR
+    return {"workload": "10 s request: 1,000 text + 72,576 video (18x48x84) + 810 audio tokens in "
+                        "1,024/72,576/832 rows, 56 heads, fused Q/K RMSNorm + partial 3D RoPE",
+            "ms_per_layer": ms, "tflops_computed_tiles": flops / (ms * 1e-3) / 1e12,
+            "steps": steps}
+
+
 def cpu_baseline(x, shape, frac, budget_rows, threads):
     """The oracle (untuned) on a bounded sample: selection + coarse for every
     row, the fine branch for a stratified sample of query rows."""
@@ -327,6 +368,8 @@ def main():
                                "fine_frac": f14 / (r14["stage_ms"][2] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         del x14, r14
     if not args.no_full_layer and args.workload == "10s_56h":
+        result["pages_request"] = pages_request(bsv, torch, np, frac, args.steps, args.warmup,
+                                                threads)
         result["full_layer"] = full_layer(bsv, torch, np, frac, max(3, args.steps // 4), 2, threads)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
