@@ -69,6 +69,11 @@ def _load():
         lib.vsa_oracle_fine_valid.restype = _I32
         lib.vsa_oracle_pool_valid.argtypes = [_P, _I32, _I64, _I64, _I64, _P, ctypes.c_int]
         lib.vsa_oracle_pool_valid.restype = None
+        lib.vsa_oracle_subblock_count.argtypes = [_I64, _F64]
+        lib.vsa_oracle_subblock_count.restype = _I32
+        lib.vsa_oracle_subblock_select.argtypes = [_P, _P, _I32, _I64, _I64, _I64, _F64, _P, _P,
+                                                   _P, _P, _P, ctypes.c_int]
+        lib.vsa_oracle_subblock_select.restype = _I32
         lib.vsa_oracle_bf16_from_f64.argtypes = [_F64]
         lib.vsa_oracle_bf16_from_f64.restype = ctypes.c_uint16
         lib.vsa_oracle_default_threads.argtypes = []
@@ -312,3 +317,36 @@ def rms_norm_rope(x: np.ndarray, gamma: np.ndarray, text_len, video_len, audio_l
     tok = (rows < vt) | is_video | ((rows >= text_len + video_len) & (rows < text_len + video_len + va))
     res[~tok] = 0
     return res
+
+
+# ---------------------------------------------------------------------------
+# SubBlock router (the C functions state the passage and the readings)
+# ---------------------------------------------------------------------------
+
+def subblock_count(n_v: int, sparsity: float) -> int:
+    """Kept video tiles per row: 8 * floor((1 - sparsity) * n_v / 8 + 1/2),
+    clamped to [min(8, n_v), n_v]; -1 for sparsity outside [0, 1).  The
+    sparsity is the C float the library receives, widened."""
+    return int(_load().vsa_oracle_subblock_count(n_v, frac_as_passed(sparsity)))
+
+
+def subblock_select(q, k, text_len, video_len, audio_len, sparsity, want_scores=False,
+                    threads=None) -> dict:
+    s = text_len + video_len + audio_len
+    h = q.shape[1]
+    q, k = (_check_tensor(x, s, h) for x in (q, k))
+    n_v = video_len // TILE
+    kk = subblock_count(n_v, sparsity)
+    if kk < 0 or video_len % TILE:
+        raise ValueError("bad arguments")
+    qsub = np.empty((h, n_v, 4, HEAD_DIM), np.float32)
+    ksub = np.empty_like(qsub)
+    sel = np.empty((h, n_v, kk), np.int32)
+    kth = np.empty((h, n_v), np.float64)
+    scores = np.empty((h, n_v, n_v), np.float64) if want_scores else None
+    r = _load().vsa_oracle_subblock_select(_ptr(q), _ptr(k), h, text_len, video_len, audio_len,
+                                           frac_as_passed(sparsity), _ptr(qsub), _ptr(ksub),
+                                           _ptr(sel), _ptr(kth), _ptr(scores), threads or 0)
+    if r < 0:
+        raise ValueError("bad arguments")
+    return {"k": kk, "qsub": qsub, "ksub": ksub, "sel": sel, "kth": kth, "scores": scores}

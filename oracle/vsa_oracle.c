@@ -493,3 +493,112 @@ int32_t vsa_oracle_fine(const uint16_t* q, const uint16_t* k, const uint16_t* v,
 
 /* Threads a call with threads <= 0 would use. */
 int32_t vsa_oracle_default_threads(void) { return resolve_threads(0); }
+
+/* ------------------------------------------------------------------------ */
+/* SubBlock router (a second selection rule feeding the same fine branch)    */
+/* ------------------------------------------------------------------------ */
+
+/* The SGLang Diffusion benchmark page, section "How SubBlock Sparse
+ * Attention Works": 64-token query and key blocks are split into four
+ * 16-token sub-blocks on both sides; a pooled log-sum-exp score estimates
+ * each key block's unnormalised softmax mass for each query block and head;
+ * the highest-scoring key blocks are kept.  The sparsity is the fraction of
+ * blocks dropped, and the kept count is rounded to whole groups of 8 blocks.
+ * Readings: the sub-block statistics are FP32 means of 16 rows (as the tile
+ * means above); the score of key tile w for query tile u is
+ *   score(u, w) = log sum_{a, b < 4} exp(alpha * qsub[u][a] . ksub[w][b]),
+ * alpha = 1/sqrt(128), dots as in pooled_score; the kept count is
+ *   k = 8 * floor((1 - sparsity) * n_v / 8 + 1/2), clamped to [min(8, n_v), n_v];
+ * ties go to the lower tile index (as the main rule).  In this path the
+ * router ranks the video key tiles of each video query tile; text and audio
+ * keys stay dense and there is no coarse term, so the fine branch is reused
+ * as it is. */
+int32_t vsa_oracle_subblock_count(int64_t n_v, double sparsity) {
+    if (!(sparsity >= 0.0 && sparsity < 1.0) || n_v < 0) return -1;
+    if (n_v == 0) return 0;
+    double k = 8.0 * floor((1.0 - sparsity) * (double)n_v / 8.0 + 0.5);
+    const double lo = n_v < 8 ? (double)n_v : 8.0;
+    if (k < lo) k = lo;
+    if (k > (double)n_v) k = (double)n_v;
+    return (int32_t)k;
+}
+
+/* FP32 means of the 16-row sub-blocks of the video tiles: out [H][n_v][4][128]. */
+static void subpool_one(const uint16_t* x, int32_t H, int64_t row0, int64_t n_v, int32_t h,
+                        int64_t u, float* out) {
+    for (int a = 0; a < 4; ++a)
+        for (int d = 0; d < D; ++d) {
+            double s = 0.0;
+            for (int r = 0; r < 16; ++r) {
+                int64_t row = row0 + u * T + 16 * a + r;
+                s += bf16_to_f64(x[(row * H + h) * D + d]);
+            }
+            out[(((int64_t)h * n_v + u) * 4 + a) * D + d] = (float)(s / 16.0);
+        }
+}
+
+typedef struct {
+    const uint16_t *q, *k;
+    int32_t H;
+    int64_t S_t, n_v;
+    int32_t kk;
+    float *qsub, *ksub;
+    int32_t* sel;
+    double* kth;
+    double* scores;
+} sub_ctx_t;
+
+static void subpool_item(void* p, int64_t item, void* scratch) {
+    (void)scratch;
+    sub_ctx_t* c = (sub_ctx_t*)p;
+    const int32_t h = (int32_t)(item / c->n_v);
+    const int64_t u = item % c->n_v;
+    subpool_one(c->q, c->H, c->S_t, c->n_v, h, u, c->qsub);
+    subpool_one(c->k, c->H, c->S_t, c->n_v, h, u, c->ksub);
+}
+
+static void subscore_item(void* p, int64_t item, void* scratch) {
+    sub_ctx_t* c = (sub_ctx_t*)p;
+    const int64_t n_v = c->n_v;
+    const int32_t h = (int32_t)(item / n_v);
+    const int64_t u = item % n_v;
+    const double alpha = 1.0 / sqrt((double)D);
+    double* s = (double*)scratch;
+    scored_t* tmp = (scored_t*)(s + n_v);
+    for (int64_t w = 0; w < n_v; ++w) {
+        double x[16], m = -INFINITY;
+        for (int a = 0; a < 4; ++a)
+            for (int b = 0; b < 4; ++b) {
+                const float* qa = c->qsub + (((int64_t)h * n_v + u) * 4 + a) * D;
+                const float* kb = c->ksub + (((int64_t)h * n_v + w) * 4 + b) * D;
+                x[4 * a + b] = alpha * pooled_score(qa, kb);
+                if (x[4 * a + b] > m) m = x[4 * a + b];
+            }
+        double e = 0.0;
+        for (int i = 0; i < 16; ++i) e += exp(x[i] - m);
+        s[w] = m + log(e);
+    }
+    if (c->scores) memcpy(c->scores + item * n_v, s, sizeof(double) * (size_t)n_v);
+    select_row(s, n_v, c->kk, tmp, c->sel + item * c->kk, c->kth ? c->kth + item : NULL);
+}
+
+/* Sub-block statistics, scores and selection for every (head, video query
+ * tile).  Outputs (caller-allocated): qsub, ksub float32 [H][n_v][4][128];
+ * sel int32 [H][n_v][k] (ascending); kth float64 [H][n_v] (k-th largest
+ * score; may be NULL); scores float64 [H][n_v][n_v] (may be NULL).
+ * Returns k, or -1 on bad arguments. */
+int32_t vsa_oracle_subblock_select(const uint16_t* q, const uint16_t* k, int32_t H, int64_t S_t,
+                                   int64_t S_v, int64_t S_a, double sparsity, float* qsub,
+                                   float* ksub, int32_t* sel, double* kth, double* scores,
+                                   int threads) {
+    if (H < 1 || S_t % T || S_v % T || S_a % T || S_t < 0 || S_v < 0 || S_a < 0) return -1;
+    const int64_t n_v = S_v / T;
+    const int32_t kk = vsa_oracle_subblock_count(n_v, sparsity);
+    if (kk < 0) return -1;
+    if (n_v == 0) return 0;
+    sub_ctx_t c = {q, k, H, S_t, n_v, kk, qsub, ksub, sel, kth, scores};
+    run_pool(subpool_item, &c, (int64_t)H * n_v, 0, threads);
+    size_t scratch = sizeof(double) * (size_t)n_v + sizeof(scored_t) * (size_t)n_v;
+    run_pool(subscore_item, &c, (int64_t)H * n_v, scratch, threads);
+    return kk;
+}

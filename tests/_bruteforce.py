@@ -74,3 +74,27 @@ def vsa_dense_masked(q, k, v, g, s_t, s_v, s_a, kk, valid=None):
         o[~tok] = 0.0
         out[:, h, :] = o
     return out, sel, coarse, masks
+
+
+def dense_masked_given_sel(q, k, v, s_t, s_v, s_a, sel):
+    """Dense attention with the video-to-video keys restricted to a given
+    selection sel [H][n_v][k] (video-local tile indices) and no coarse term:
+    the attention that a selection rule other than the tile score (for
+    instance the SubBlock router) hands to the block-sparse kernel.
+    Returns float64 [S][H][128]."""
+    Q, K, V = (widen(x) for x in (q, k, v))
+    S, H, _ = Q.shape
+    n_t = s_t // T
+    tile_of = np.arange(S) // T
+    key_is_video = (np.arange(S) >= s_t) & (np.arange(S) < s_t + s_v)
+    alpha = 1.0 / np.sqrt(D)
+    out = np.zeros((S, H, D))
+    for h in range(H):
+        mask = np.ones((S, S), dtype=bool)
+        for i in range(s_t, s_t + s_v):
+            allowed = n_t + np.asarray(sel[h, (i - s_t) // T])
+            mask[i] = ~key_is_video | np.isin(tile_of, allowed)
+        logits = np.where(mask, alpha * (Q[:, h, :] @ K[:, h, :].T), -np.inf)
+        p = np.exp(logits - logits.max(axis=1, keepdims=True))
+        out[:, h, :] = (p @ V[:, h, :]) / p.sum(axis=1, keepdims=True)
+    return out
