@@ -39,6 +39,7 @@ D = 128
 FLOP_PER_PAIR = 4 * TILE * TILE * D          # QK^T + PV of one 64x64 tile pair
 PEAK_BF16_TFLOPS = 2500.0                   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E (published)
+PEAK_FP64_TFLOPS = 78.6                     # MI355X dense fp64 MFMA (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fine_attn_traffic_10s_56h.txt")
 FINE_SOURCE = os.path.join(ROOT, "block_sparse_video_amd", "csrc", "fine_attn.hip")
 
@@ -227,6 +228,44 @@ def pages_request(bsv, torch, np, frac, steps, warmup, threads):
             "steps": steps}
 
 
+SUBBLOCK_SPARSITY = 0.75
+
+
+def subblock_leg(bsv, torch, xd, shape, steps, warmup):
+    """The same inputs through the SubBlock router path (vsa_forward_subblock,
+    sparsity 0.75 -> 280 of 1,134 video tiles kept per query tile): the router
+    stage alone (sub-block means + float64 MFMA scores + top-k) and the whole
+    forward, timed with HIP events on the current stream."""
+    h, s_t, s_v, s_a = shape
+    sp = SUBBLOCK_SPARSITY
+    out, sel, ws = bsv.alloc_subblock_outputs(h, s_t, s_v, s_a, sp)
+    q, k, v = xd["q"], xd["k"], xd["v"]
+    for _ in range(warmup):
+        bsv.vsa_forward_subblock(q, k, v, s_t, s_v, s_a, sp, out, sel, ws)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(steps):
+        bsv.vsa_subblock_select(q, k, s_t, s_v, s_a, sp, sel, ws)
+    ev[1].record(stream)
+    for _ in range(steps):
+        bsv.vsa_forward_subblock(q, k, v, s_t, s_v, s_a, sp, out, sel, ws)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    sel_ms = ev[0].elapsed_time(ev[1]) / steps
+    fwd_ms = ev[1].elapsed_time(ev[2]) / steps
+    kk = bsv.vsa_subblock_count(s_v, sp)
+    n_v = s_v // TILE
+    route_flop = 2.0 * h * (4 * n_v) ** 2 * D  # float64 MFMA work of the scores
+    flops = tile_pairs(h, s_t, s_v, s_a, kk) * FLOP_PER_PAIR
+    return {"workload": f"SubBlock router path, same inputs, sparsity {sp} (k={kk})",
+            "k": kk, "router_ms": sel_ms, "router_fp64_tflops": route_flop / (sel_ms * 1e-3) / 1e12,
+            "router_fp64_frac": route_flop / (sel_ms * 1e-3) / 1e12 / PEAK_FP64_TFLOPS,
+            "ms_per_layer": fwd_ms, "tflops_computed_tiles": flops / (fwd_ms * 1e-3) / 1e12,
+            "steps": steps}
+
+
 def cpu_baseline(x, shape, frac, budget_rows, threads):
     """The oracle (untuned) on a bounded sample: selection + coarse for every
     row, the fine branch for a stratified sample of query rows."""
@@ -276,6 +315,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-full-layer", action="store_true",
                     help="skip the full-layer run (Q/K/V/gate projections + VSA on smooth video fields)")
+    ap.add_argument("--no-subblock", action="store_true", help="skip the SubBlock router leg")
     ap.add_argument("--cpu-rows", type=int, default=48, help="video tiles in the oracle sample")
     ap.add_argument("--threads", type=int, default=None, help="oracle / generator threads")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -367,6 +407,8 @@ def main():
                                "fine_attn_ms": r14["stage_ms"][2],
                                "fine_frac": f14 / (r14["stage_ms"][2] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         del x14, r14
+    if not args.no_subblock and args.workload == "10s_56h":
+        result["subblock"] = subblock_leg(bsv, torch, xd, shape, args.steps, args.warmup)
     if not args.no_full_layer and args.workload == "10s_56h":
         result["pages_request"] = pages_request(bsv, torch, np, frac, args.steps, args.warmup,
                                                 threads)

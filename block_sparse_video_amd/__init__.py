@@ -18,7 +18,8 @@ TILE = 64
 
 __all__ = ["vsa_topk_count", "vsa_workspace_bytes", "vsa_workspace_layout", "vsa_forward",
            "vsa_pool_pack", "vsa_select_coarse", "vsa_fine_attention", "forward", "VsaError",
-           "status_string", "LIB_PATH"]
+           "status_string", "LIB_PATH", "vsa_subblock_count", "vsa_subblock_workspace_bytes",
+           "vsa_forward_subblock", "vsa_subblock_select", "forward_subblock"]
 
 
 def _torch():
@@ -209,3 +210,69 @@ def vsa_forward_padded(q, k, v, gate, text_len, video_len, audio_len, valid, top
                                      workspace.numel() if workspace is not None else 0,
                                      _stream(stream)),
            "vsa_forward_padded")
+
+
+# ---------------------------------------------------------------------------
+# SubBlock router: 16-token sub-block log-sum-exp scores choose the video key
+# tiles; no coarse branch, no gate.
+# ---------------------------------------------------------------------------
+
+def vsa_subblock_count(video_len: int, sparsity: float) -> int:
+    return int(load().vsa_subblock_count(video_len, sparsity))
+
+
+def vsa_subblock_workspace_bytes(num_heads: int, text_len: int, video_len: int,
+                                 audio_len: int) -> int:
+    return int(load().vsa_subblock_workspace_bytes(num_heads, text_len, video_len, audio_len))
+
+
+def vsa_forward_subblock(q, k, v, text_len, video_len, audio_len, sparsity, out, selected_tiles,
+                         workspace=None, stream=None):
+    torch = _torch()
+    shp = _shape_args(q, text_len, video_len, audio_len)
+    q, k, v, out = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k"), (v, "v"),
+                                                                    (out, "out")))
+    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32)
+    workspace = _tensor(workspace, "workspace", torch.uint8)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(load().vsa_forward_subblock(_ptr(q), _ptr(k), _ptr(v), shp[1], text_len, video_len,
+                                       audio_len, sparsity, _ptr(out), _ptr(selected_tiles),
+                                       _ptr(workspace), nbytes, _stream(stream)),
+           "vsa_forward_subblock")
+
+
+def vsa_subblock_select(q, k, text_len, video_len, audio_len, sparsity, selected_tiles, workspace,
+                        stream=None):
+    torch = _torch()
+    shp = _shape_args(q, text_len, video_len, audio_len)
+    q, k = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k")))
+    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32)
+    workspace = _tensor(workspace, "workspace", torch.uint8)
+    _check(load().vsa_subblock_select(_ptr(q), _ptr(k), shp[1], text_len, video_len, audio_len,
+                                      sparsity, _ptr(selected_tiles), _ptr(workspace),
+                                      workspace.numel(), _stream(stream)), "vsa_subblock_select")
+
+
+def alloc_subblock_outputs(num_heads, text_len, video_len, audio_len, sparsity, device=None):
+    """Allocate (out, selected_tiles, workspace) for vsa_forward_subblock."""
+    torch = _torch()
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    s = text_len + video_len + audio_len
+    kk = vsa_subblock_count(video_len, sparsity)
+    wsb = vsa_subblock_workspace_bytes(num_heads, text_len, video_len, audio_len)
+    if kk < 0 or wsb == 0:
+        raise ValueError("bad shape or sparsity")
+    out = torch.empty((s, num_heads, HEAD_DIM), dtype=torch.bfloat16, device=device)
+    sel = torch.empty((num_heads, video_len // TILE, kk), dtype=torch.int32, device=device)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=device)
+    return out, sel, ws
+
+
+def forward_subblock(q, k, v, text_len, video_len, audio_len, sparsity=0.75, workspace=None,
+                     stream=None):
+    """Convenience wrapper of vsa_forward_subblock (allocates with torch)."""
+    out, sel, ws = alloc_subblock_outputs(q.shape[1], text_len, video_len, audio_len, sparsity,
+                                          q.device)
+    vsa_forward_subblock(q, k, v, text_len, video_len, audio_len, sparsity, out, sel,
+                         workspace if workspace is not None else ws, stream)
+    return out, sel

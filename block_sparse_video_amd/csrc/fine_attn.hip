@@ -1,6 +1,7 @@
 // fine_attn.hip -- stage 3 of the VSA forward on gfx950: block-sparse flash
 // attention over 64x64 tiles with bf16 MFMA, online softmax in fp32, and the
-// gated coarse combination fused into the epilogue.
+// gated coarse combination fused into the epilogue (none when gate is NULL:
+// selections of the SubBlock router carry no coarse term).
 //
 // Page "UniServe: serving FastH3 at its fastest":
 //   section "The FastH3 workload": text and audio query tiles attend to every
@@ -468,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         if (row >= nq) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] = 0.0f;
-        } else if (video) {
+        } else if (video && a.gate) {
             const uint4 gw = *(const uint4*)(a.gate + grow * rs + (int64_t)h * kD + 8 * c);
             const float4 c0 = *(const float4*)(cp + 8 * c);
             const float4 c1 = *(const float4*)(cp + 8 * c + 4);

@@ -53,6 +53,19 @@ int32_t topk_count(int64_t n_v, float frac) {
     return (int32_t)k;
 }
 
+// SubBlock router kept count: whole groups of 8 tiles, at least one group
+// (or every tile when there are fewer than 8), at most n_v.
+int32_t subblock_count(int64_t n_v, float sparsity) {
+    const double f = (double)sparsity;
+    if (!(f >= 0.0 && f < 1.0) || n_v < 0) return -1;
+    if (n_v == 0) return 0;
+    double k = 8.0 * std::floor((1.0 - f) * (double)n_v / 8.0 + 0.5);
+    const double lo = n_v < 8 ? (double)n_v : 8.0;
+    if (k < lo) k = lo;
+    if (k > (double)n_v) k = (double)n_v;
+    return (int32_t)k;
+}
+
 vsa_status check_topk(float frac, Shape* s) {
     const int32_t k = topk_count(s->n_v, frac);
     if (k < 0) return VSA_ERR_BAD_TOPK;
@@ -306,6 +319,79 @@ vsa_status vsa_forward_padded(const void* q, const void* k, const void* v, const
                                        (const uint16_t*)gate, selected_tiles, (uint16_t*)out, s, ws,
                                        L, strm);
     return from_hip(e);
+}
+
+int32_t vsa_subblock_count(int64_t video_len, float sparsity) {
+    if (video_len < 0 || video_len % VSA_TILE) return -1;
+    return subblock_count(video_len / VSA_TILE, sparsity);
+}
+
+size_t vsa_subblock_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_len,
+                                    int64_t audio_len) {
+    Shape s;
+    if (make_shape(num_heads, text_len, video_len, audio_len, &s) != VSA_OK) return 0;
+    if (s.n_v > vsa::kSubblockMaxTiles) return 0;
+    return vsa::make_layout(s, true).total;
+}
+
+vsa_status vsa_forward_subblock(const void* q, const void* k, const void* v, int32_t num_heads,
+                                int64_t text_len, int64_t video_len, int64_t audio_len,
+                                float sparsity, void* out, int32_t* selected_tiles,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !out) return VSA_ERR_NULL_POINTER;
+    if (video_len != 0 && !selected_tiles) return VSA_ERR_NULL_POINTER;
+    Shape s;
+    vsa_status st = make_shape(num_heads, text_len, video_len, audio_len, &s);
+    if (st != VSA_OK) return st;
+    if (s.n_v > vsa::kSubblockMaxTiles) return VSA_ERR_TOO_LARGE;
+    const int32_t kk = subblock_count(s.n_v, sparsity);
+    if (kk < 0) return VSA_ERR_BAD_TOPK;
+    s.k = kk;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        (selected_tiles && !aligned(selected_tiles, 16)))
+        return VSA_ERR_MISALIGNED;
+    const Layout L = vsa::make_layout(s, true);
+    if (workspace) {
+        if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
+    }
+    if ((st = check_device()) != VSA_OK) return st;
+    if (!workspace) {
+        if ((st = owned_workspace(L.total, &workspace)) != VSA_OK) return st;
+    }
+    hipStream_t strm = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    hipError_t e = vsa::launch_pool_pack((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                         s, ws, L, strm);
+    if (e == hipSuccess)
+        e = vsa::launch_subblock_route((const uint16_t*)q, (const uint16_t*)k, s, selected_tiles,
+                                       ws, L, strm);
+    if (e == hipSuccess)
+        e = vsa::launch_fine_attention((const uint16_t*)q, nullptr, selected_tiles,
+                                       (uint16_t*)out, s, ws, L, strm);
+    return from_hip(e);
+}
+
+vsa_status vsa_subblock_select(const void* q, const void* k, int32_t num_heads, int64_t text_len,
+                               int64_t video_len, int64_t audio_len, float sparsity,
+                               int32_t* selected_tiles, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (!q || !k || !selected_tiles) return VSA_ERR_NULL_POINTER;
+    Shape s;
+    vsa_status st = make_shape(num_heads, text_len, video_len, audio_len, &s);
+    if (st != VSA_OK) return st;
+    if (s.n_v == 0) return VSA_ERR_BAD_SHAPE;
+    if (s.n_v > vsa::kSubblockMaxTiles) return VSA_ERR_TOO_LARGE;
+    const int32_t kk = subblock_count(s.n_v, sparsity);
+    if (kk < 0) return VSA_ERR_BAD_TOPK;
+    s.k = kk;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(selected_tiles, 16))
+        return VSA_ERR_MISALIGNED;
+    const Layout L = vsa::make_layout(s, true);
+    if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
+    if ((st = check_device()) != VSA_OK) return st;
+    return from_hip(vsa::launch_subblock_route((const uint16_t*)q, (const uint16_t*)k, s,
+                                               selected_tiles, (uint8_t*)workspace, L,
+                                               (hipStream_t)stream));
 }
 
 vsa_status vsa_project_qkvg(const void* x, const void* w, int64_t tokens, int32_t hidden,

@@ -179,6 +179,61 @@ vsa_status vsa_forward_padded(const void* q, const void* k, const void* v, const
                               int32_t* selected_tiles, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* SubBlock router (the SGLang Diffusion benchmark page, section "How
+ * SubBlock Sparse Attention Works"): a second rule for choosing each video
+ * query tile's video key tiles, fed to the same fine attention.  Every
+ * 64-token tile is split into four 16-token sub-blocks; per head, video
+ * query tile u and video key tile w,
+ *   x_ab = dot(mean Q of sub-block a of u, mean K of sub-block b of w) / sqrt(128)
+ *          (means of 16 rows as float32, dots and everything after in float64)
+ *   score(u, w) = log sum over the 16 pairs (a, b) of exp(x_ab),
+ * which estimates the unnormalised softmax mass of key tile w for query tile
+ * u.  The kept count is vsa_subblock_count(video_len, sparsity); ties in the
+ * ranking go to the lower tile index.  Text and audio queries attend to every
+ * key, video queries to every text and audio key and to their kept video
+ * tiles; there is no coarse branch and no gate (out = O_fine).
+ *
+ * vsa_subblock_count: sparsity is the fraction of video tiles dropped,
+ * 0 <= sparsity < 1; the kept count is rounded to whole groups of 8 tiles:
+ *   k = 8 * floor((1 - sparsity) * n_v / 8 + 1/2)   (double arithmetic),
+ * clamped to [min(8, n_v), n_v]; 0 when video_len == 0.  Returns -1 if
+ * video_len is negative or not a multiple of 64, or sparsity is out of range.
+ * Host only. */
+int32_t vsa_subblock_count(int64_t video_len, float sparsity);
+
+/* Workspace bytes of vsa_forward_subblock; 0 if the shape is invalid or
+ * n_v exceeds VSA_SUBBLOCK_MAX_VIDEO_TILES.  Its first vsa_workspace_bytes()
+ * bytes are laid out as vsa_workspace_layout() states; the Q sub-block means
+ * follow, then the K sub-block means, each float32, 8 KiB per (head, group of
+ * 4 video tiles), at the next 256-byte boundaries.  Host only. */
+#define VSA_SUBBLOCK_MAX_VIDEO_TILES 5120
+size_t vsa_subblock_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_len,
+                                    int64_t audio_len);
+
+/* The VSA forward with the SubBlock router in place of the tile score and the
+ * coarse branch.  q, k, v, out: bf16 [S][H][128] as vsa_forward;
+ * selected_tiles: int32 [H][n_v][k], k = vsa_subblock_count(video_len,
+ * sparsity), ascending video-local indices (may be NULL only when video_len
+ * is 0).  Padding rows are not supported here (every row is a token).
+ * n_v <= VSA_SUBBLOCK_MAX_VIDEO_TILES (VSA_ERR_TOO_LARGE otherwise); a bad
+ * sparsity returns VSA_ERR_BAD_TOPK.  workspace: NULL (library-owned) or at
+ * least vsa_subblock_workspace_bytes(...) bytes, 256-byte aligned.
+ * Everything else as vsa_forward. */
+vsa_status vsa_forward_subblock(const void* q, const void* k, const void* v, int32_t num_heads,
+                                int64_t text_len, int64_t video_len, int64_t audio_len,
+                                float sparsity, void* out, int32_t* selected_tiles,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* The router stage of vsa_forward_subblock alone: sub-block means of Q and K
+ * into the workspace, scores and selection into selected_tiles.  Requires
+ * video_len > 0 (VSA_ERR_BAD_SHAPE otherwise) and a caller workspace of
+ * vsa_subblock_workspace_bytes(...) bytes.  Other arguments and errors as
+ * vsa_forward_subblock. */
+vsa_status vsa_subblock_select(const void* q, const void* k, int32_t num_heads, int64_t text_len,
+                               int64_t video_len, int64_t audio_len, float sparsity,
+                               int32_t* selected_tiles, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 /* The Q, K, V and gate projections that produce this path's inputs (page
  * "UniServe: serving FastH3 at its fastest", section "The FastH3 workload":
  * hidden size 5,376, 56 heads of 128, so each projection maps 5,376 channels

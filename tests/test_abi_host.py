@@ -130,3 +130,59 @@ def test_project_validation():
     assert lib.vsa_project_qkvg(FAKE + 2, FAKE, 4, 64, 2, *o, None) == MISALIGNED
     assert lib.vsa_project_qkvg(FAKE, FAKE, 4, 32768, 2, *o, None) == TOO_LARGE
     assert lib.vsa_project_qkvg(FAKE, FAKE, 4, 64, 2048, *o, None) == TOO_LARGE
+
+
+def test_subblock_count_matches_oracle():
+    import oracle
+    for n_v in (0, 1, 5, 7, 8, 9, 15, 16, 17, 100, 640, 1134, 5120):
+        for sp in (0.0, 0.1, 0.5, 0.75, 0.8, 0.875, 0.9, 0.95, 0.999):
+            assert bsv.vsa_subblock_count(64 * n_v, sp) == oracle.subblock_count(n_v, sp), (n_v, sp)
+    assert bsv.vsa_subblock_count(1134 * 64, 0.75) == 280
+    for bad in (1.0, -0.01, float("nan"), float("inf")):
+        assert bsv.vsa_subblock_count(640, bad) == -1
+    assert bsv.vsa_subblock_count(65, 0.5) == -1
+
+
+def test_subblock_workspace_bytes():
+    base = bsv.vsa_workspace_bytes(56, 1024, 72576, 1024)
+    n = bsv.vsa_subblock_workspace_bytes(56, 1024, 72576, 1024)
+    # Q and K sub-block means, 8 KiB per (head, group of 4 video tiles), 256-byte aligned
+    assert n == base + 2 * (56 * 284 * 8192)
+    assert bsv.vsa_subblock_workspace_bytes(1, 0, 64 * 5120, 0) > 0
+    assert bsv.vsa_subblock_workspace_bytes(1, 0, 64 * 5121, 0) == 0
+    assert bsv.vsa_subblock_workspace_bytes(1, 0, 65, 0) == 0
+
+
+def test_subblock_forward_validation():
+    lib = _native.load()
+    f = lib.vsa_forward_subblock
+    args = dict(q=FAKE, k=FAKE, v=FAKE, h=2, t=64, vid=640, au=64, sp=0.75, out=FAKE, sel=FAKE,
+                ws=FAKE, wsb=1 << 40)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["k"], a["v"], a["h"], a["t"], a["vid"], a["au"], a["sp"], a["out"],
+                 a["sel"], a["ws"], a["wsb"], None)
+    assert call(q=None) == NULLP
+    assert call(sel=None) == NULLP
+    assert call(vid=0, sel=None, wsb=10) == WORKSPACE
+    assert call(h=0) == SHAPE
+    assert call(vid=100) == UNALIGNED
+    assert call(sp=1.0) == TOPK
+    assert call(sp=-0.5) == TOPK
+    assert call(vid=64 * 5121) == TOO_LARGE
+    assert call(out=FAKE + 2) == MISALIGNED
+    assert call(sel=FAKE + 4) == MISALIGNED
+    assert call(ws=FAKE + 16) == MISALIGNED
+    assert call(wsb=bsv.vsa_workspace_bytes(2, 64, 640, 64)) == WORKSPACE
+
+
+def test_subblock_select_validation():
+    f = _native.load().vsa_subblock_select
+    assert f(None, FAKE, 2, 64, 640, 64, 0.75, FAKE, FAKE, 1 << 40, None) == NULLP
+    assert f(FAKE, FAKE, 2, 64, 640, 64, 0.75, None, FAKE, 1 << 40, None) == NULLP
+    assert f(FAKE, FAKE, 2, 64, 0, 64, 0.75, FAKE, FAKE, 1 << 40, None) == SHAPE
+    assert f(FAKE, FAKE, 2, 64, 640, 64, 1.5, FAKE, FAKE, 1 << 40, None) == TOPK
+    assert f(FAKE, FAKE, 2, 64, 640, 64, 0.75, FAKE, None, 1 << 40, None) == WORKSPACE
+    assert f(FAKE, FAKE, 2, 64, 640, 64, 0.75, FAKE, FAKE, 64, None) == WORKSPACE
+    assert f(FAKE, FAKE, 2, 64, 64 * 6000, 64, 0.75, FAKE, FAKE, 1 << 40, None) == TOO_LARGE

@@ -210,3 +210,17 @@ def test_fine_with_router_selection_matches_dense_masked():
                          np.zeros((h, n_v, D)), np.arange(s))
     want = bf.dense_masked_given_sel(q, k, v, s_t, s_v, s_a, r["sel"])
     np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-12)
+
+
+def test_row_subset_matches_all_rows():
+    rng = np.random.default_rng(16)
+    h, n_v = 3, 21
+    s = T * (n_v + 2)
+    q, k = (_bits(rng.standard_normal((s, h, D))) for _ in range(2))
+    full = oracle.subblock_select(q, k, T, T * n_v, T, 0.6, want_scores=True)
+    rows = [(2, 20), (0, 0), (1, 7), (2, 3)]
+    part = oracle.subblock_select_rows(q, k, T, T * n_v, T, 0.6, rows)
+    for i, (hh, u) in enumerate(rows):
+        np.testing.assert_array_equal(part["sel"][i], full["sel"][hh, u])
+        np.testing.assert_array_equal(part["scores"][i], full["scores"][hh, u])
+    np.testing.assert_array_equal(part["qsub"], full["qsub"])
