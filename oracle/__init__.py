@@ -74,6 +74,9 @@ def _load():
         lib.vsa_oracle_subblock_select.argtypes = [_P, _P, _I32, _I64, _I64, _I64, _F64, _P, _P,
                                                    _P, _P, _P, ctypes.c_int]
         lib.vsa_oracle_subblock_select.restype = _I32
+        lib.vsa_oracle_subblock_select_rows.argtypes = [_P, _P, _I32, _I64, _I64, _I64, _F64, _P,
+                                                        _I64, _P, _P, _P, _P, _P, ctypes.c_int]
+        lib.vsa_oracle_subblock_select_rows.restype = _I32
         lib.vsa_oracle_bf16_from_f64.argtypes = [_F64]
         lib.vsa_oracle_bf16_from_f64.restype = ctypes.c_uint16
         lib.vsa_oracle_default_threads.argtypes = []
@@ -347,6 +350,34 @@ def subblock_select(q, k, text_len, video_len, audio_len, sparsity, want_scores=
     r = _load().vsa_oracle_subblock_select(_ptr(q), _ptr(k), h, text_len, video_len, audio_len,
                                            frac_as_passed(sparsity), _ptr(qsub), _ptr(ksub),
                                            _ptr(sel), _ptr(kth), _ptr(scores), threads or 0)
+    if r < 0:
+        raise ValueError("bad arguments")
+    return {"k": kk, "qsub": qsub, "ksub": ksub, "sel": sel, "kth": kth, "scores": scores}
+
+
+def subblock_select_rows(q, k, text_len, video_len, audio_len, sparsity, rows, threads=None) -> dict:
+    """subblock_select for the (head, video tile) rows listed as pairs; the
+    sub-block means cover every tile.  Returns qsub, ksub [H][n_v][4][128],
+    sel [n][k], kth [n], scores [n][n_v]."""
+    s = text_len + video_len + audio_len
+    h = q.shape[1]
+    q, k = (_check_tensor(x, s, h) for x in (q, k))
+    n_v = video_len // TILE
+    kk = subblock_count(n_v, sparsity)
+    if kk < 0 or video_len % TILE:
+        raise ValueError("bad arguments")
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+    flat = np.ascontiguousarray(rows[:, 0] * n_v + rows[:, 1])
+    n = len(flat)
+    qsub = np.empty((h, n_v, 4, HEAD_DIM), np.float32)
+    ksub = np.empty_like(qsub)
+    sel = np.empty((n, kk), np.int32)
+    kth = np.empty(n, np.float64)
+    scores = np.empty((n, n_v), np.float64)
+    r = _load().vsa_oracle_subblock_select_rows(_ptr(q), _ptr(k), h, text_len, video_len,
+                                                audio_len, frac_as_passed(sparsity), _ptr(flat), n,
+                                                _ptr(qsub), _ptr(ksub), _ptr(sel), _ptr(kth),
+                                                _ptr(scores), threads or 0)
     if r < 0:
         raise ValueError("bad arguments")
     return {"k": kk, "qsub": qsub, "ksub": ksub, "sel": sel, "kth": kth, "scores": scores}

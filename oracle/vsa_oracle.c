@@ -546,6 +546,7 @@ typedef struct {
     int32_t* sel;
     double* kth;
     double* scores;
+    const int64_t* rows;  /* NULL: every (head, tile) in order; else rows[i] = h * n_v + u */
 } sub_ctx_t;
 
 static void subpool_item(void* p, int64_t item, void* scratch) {
@@ -560,8 +561,9 @@ static void subpool_item(void* p, int64_t item, void* scratch) {
 static void subscore_item(void* p, int64_t item, void* scratch) {
     sub_ctx_t* c = (sub_ctx_t*)p;
     const int64_t n_v = c->n_v;
-    const int32_t h = (int32_t)(item / n_v);
-    const int64_t u = item % n_v;
+    const int64_t hu = c->rows ? c->rows[item] : item;
+    const int32_t h = (int32_t)(hu / n_v);
+    const int64_t u = hu % n_v;
     const double alpha = 1.0 / sqrt((double)D);
     double* s = (double*)scratch;
     scored_t* tmp = (scored_t*)(s + n_v);
@@ -596,9 +598,33 @@ int32_t vsa_oracle_subblock_select(const uint16_t* q, const uint16_t* k, int32_t
     const int32_t kk = vsa_oracle_subblock_count(n_v, sparsity);
     if (kk < 0) return -1;
     if (n_v == 0) return 0;
-    sub_ctx_t c = {q, k, H, S_t, n_v, kk, qsub, ksub, sel, kth, scores};
+    sub_ctx_t c = {q, k, H, S_t, n_v, kk, qsub, ksub, sel, kth, scores, NULL};
     run_pool(subpool_item, &c, (int64_t)H * n_v, 0, threads);
     size_t scratch = sizeof(double) * (size_t)n_v + sizeof(scored_t) * (size_t)n_v;
     run_pool(subscore_item, &c, (int64_t)H * n_v, scratch, threads);
+    return kk;
+}
+
+/* As vsa_oracle_subblock_select, for the listed rows only (rows[i] = h * n_v
+ * + u): sub-block means of every tile (qsub, ksub as above), then scores and
+ * selection of n_rows rows: sel [n_rows][k], kth [n_rows], scores [n_rows][n_v]
+ * (may be NULL).  Returns k, or -1 on bad arguments. */
+int32_t vsa_oracle_subblock_select_rows(const uint16_t* q, const uint16_t* k, int32_t H,
+                                        int64_t S_t, int64_t S_v, int64_t S_a, double sparsity,
+                                        const int64_t* rows, int64_t n_rows, float* qsub,
+                                        float* ksub, int32_t* sel, double* kth, double* scores,
+                                        int threads) {
+    if (H < 1 || S_t % T || S_v % T || S_a % T || S_t < 0 || S_v < 0 || S_a < 0 || n_rows < 0)
+        return -1;
+    const int64_t n_v = S_v / T;
+    const int32_t kk = vsa_oracle_subblock_count(n_v, sparsity);
+    if (kk < 0) return -1;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= (int64_t)H * n_v) return -1;
+    if (n_v == 0) return 0;
+    sub_ctx_t c = {q, k, H, S_t, n_v, kk, qsub, ksub, sel, kth, scores, rows};
+    run_pool(subpool_item, &c, (int64_t)H * n_v, 0, threads);
+    size_t scratch = sizeof(double) * (size_t)n_v + sizeof(scored_t) * (size_t)n_v;
+    run_pool(subscore_item, &c, n_rows, scratch, threads);
     return kk;
 }
