@@ -117,16 +117,33 @@ def time_path(bsv, torch, xd, shape, frac, steps, warmup):
     wall = time.perf_counter() - t0
     total_ms = ev[0][0].elapsed_time(ev[-1][3]) / steps
     stage = [sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps for j in range(3)]
-    # the fused entry point, same work, for reference
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
+    # the fused entry point, same work, one event pair per call
+    fe = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    fe[0].record(stream)
+    for i in range(steps):
         bsv.vsa_forward(q, k, v, g, s_t, s_v, s_a, frac, out, sel, ws)
-    e1.record(stream)
+        fe[i + 1].record(stream)
     torch.cuda.synchronize()
-    fwd_ms = e0.elapsed_time(e1) / steps
+    per_call = sorted(fe[i].elapsed_time(fe[i + 1]) for i in range(steps))
+    fwd_ms = sum(per_call) / steps
+    stats = {"median": per_call[steps // 2] if steps % 2 else
+             0.5 * (per_call[steps // 2 - 1] + per_call[steps // 2]),
+             "min": per_call[0], "p90": per_call[min(steps - 1, int(0.9 * steps))]}
     return {"ms": total_ms, "wall_ms": wall * 1e3 / steps, "stage_ms": stage, "forward_ms": fwd_ms,
-            "out": out, "sel": sel}
+            "forward_stats": stats, "out": out, "sel": sel}
+
+
+def device_clock_mhz():
+    """Peak shader clock the runtime reports (hipDeviceAttributeClockRate, kHz)."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        val = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(val), 5, 0) == 0:
+            return val.value / 1000.0
+    except OSError:
+        pass
+    return None
 
 
 FULL_LAYER = dict(text_len=1024, grid=(18, 48, 84), audio_len=1024, hidden=5376, heads=56)
@@ -391,10 +408,17 @@ def main():
             "select_coarse_ms": r["stage_ms"][1],
             "fine_attn_ms": fine_ms,
             "forward_entry_ms": r["forward_ms"],
+            "forward_entry_ms_median_min_p90": [r["forward_stats"]["median"],
+                                                r["forward_stats"]["min"],
+                                                r["forward_stats"]["p90"]],
             "host_wall_ms_per_step": r["wall_ms"],
         },
         "device": {"name": prop.name, "cus": prop.multi_processor_count,
-                   "arch": getattr(prop, "gcnArchName", "")},
+                   "arch": getattr(prop, "gcnArchName", ""),
+                   "peak_clock_mhz": device_clock_mhz(),
+                   "peak_used": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS,
+                                 "fp64_mfma_tflops": PEAK_FP64_TFLOPS,
+                                 "hbm_gbs": PEAK_HBM_GBS}},
     }
     del r
     if not args.no_secondary and h == 56:
