@@ -160,6 +160,15 @@ __device__ __forceinline__ void fetch_half(uint32_t slot, const char* base, cons
         : "memory", "m0", "scc");
 }
 
+// One 1 KiB piece of a half-tile copy: LDS bytes ldsaddr + 16 lane .. +15
+// from global base + voff (voff = 16 lane + 1024 i for piece i).
+__device__ __forceinline__ void fetch_piece(uint32_t ldsaddr, const char* base, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %[s]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v], %[b]"
+                 :
+                 : [s] "s"(ldsaddr), [b] "s"(base), [v] "v"(voff)
+                 : "memory", "m0");
+}
+
 // Wait until at most n of this wave's vector-memory loads are outstanding
 // (s_waitcnt encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt at
 // their "no wait" maxima).  The compiler does not track the LDS writes of
@@ -322,11 +331,14 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         //   O       += V(x-1) P(x-1)            (16 MFMAs)
         // so none of its matrix work waits for its own vector work.  Operands
         // enter registers one step ahead (K(x+2) in the middle of step x,
-        // V(x) at its end).  Step x fetches V(x+1) and then K(x+4), so a K
-        // half-tile has two and a half steps to arrive and a V half-tile two.
-        // In issue order, everything up to K(x+2) is complete once at most 32
-        // fetches are outstanding (V(x), K(x+3) of step x-1 and this step's
-        // two), and everything up to V(x) once at most 24 are.
+        // V(x) at its end).  Step x fetches V(x+1), one 1 KiB piece after
+        // each pair of S^T MFMAs, and then K(x+4), one piece after each pair
+        // of PV MFMAs, so the copies issue while the matrix unit is busy; a
+        // K half-tile has about two steps to arrive and a V half-tile two.
+        // In issue order, K(x+2) is complete once at most 24 fetches are
+        // outstanding at the middle of the step (V(x), K(x+3) of step x-1 and
+        // V(x+1)), and V(x) once at most 24 are at its end (K(x+3), V(x+1),
+        // K(x+4)).
         bf16x8 kop[8], vop[8];
         bf16x8 pprev[2][2];
         f32x16 sc[2];
@@ -378,9 +390,11 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
                 const int k_wr = xm3 == 2 ? 0 : xm3 + 1;  // (x + 4) mod 3
                 const int k_rd = xm3 == 0 ? 2 : xm3 - 1;  // (x + 2) mod 3
                 wait_lgkm();  // kop = K(x+1), vop = V(x-1)
-                // V(x+1): (t, half 1) or (t+1, half 0); K(x+4): (t+2, half pp)
-                fetch_v(vslot[pp ^ 1], pp == 0 ? cur : nxt, pp ^ 1);
-                fetch_k(kslot(k_wr), nn, pp);
+                // V(x+1): (t, half 1) or (t+1, half 0); K(x+4): (t+2, half pp),
+                // issued one 1 KiB piece at a time between MFMAs below
+                const char* vsrc = vbase + (pp == 0 ? cur : nxt) * kTileBytes + (pp ^ 1) * kHalfBytes;
+                const char* ksrc = kbase + nn * kTileBytes + pp * kHalfBytes;
+                const uint32_t vdst = vslot[pp ^ 1], kdst = kslot(k_wr);
                 f32x16 n0 = zero16, n1 = zero16;
                 bf16x8 pc[2][2];
                 {
@@ -395,9 +409,11 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
                 for (int s8 = 0; s8 < 8; ++s8) {
                     n0 = mfma32(kop[s8], qf[0][s8], n0);
                     n1 = mfma32(kop[s8], qf[1][s8], n1);
+                    fetch_piece(vdst + 1024u * s8, vsrc, voff[s8]);
+                    __builtin_amdgcn_sched_barrier(0x406);
                 }
                 numerators(sc[0], c2, m_ref[0], l_run[0], pc[0][0], pc[0][1]);
-                wait_vmcnt(32);  // K(x+2)
+                wait_vmcnt(24);  // K(x+2)
                 read_ops(kop, kslot(k_rd), lane);
 #pragma unroll
                 for (int db = 0; db < 4; ++db)
@@ -405,6 +421,8 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
                     for (int m = 0; m < 2; ++m) {
                         o[0][db] = mfma32(vop[2 * db + m], pprev[0][m], o[0][db]);
                         o[1][db] = mfma32(vop[2 * db + m], pprev[1][m], o[1][db]);
+                        fetch_piece(kdst + 1024u * (2 * db + m), ksrc, voff[2 * db + m]);
+                        __builtin_amdgcn_sched_barrier(0x406);
                     }
                 numerators(sc[1], c2, m_ref[1], l_run[1], pc[1][0], pc[1][1]);
                 wait_vmcnt(24);  // V(x)

@@ -9,18 +9,18 @@
 // the contracted dimension and out_p is token-major [S][H][128], the layout
 // the attention stages read.
 //
-// Tiling.  One workgroup (4 wavefronts) computes 256 output channels x 256
-// tokens; wavefront (wf, wt) owns channels 128 wf .. +127 and tokens
-// 128 wt .. +127 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 (channels are
-// the MFMA rows, tokens its columns, so each lane ends with runs of four
+// Tiling.  One workgroup (8 wavefronts, two per SIMD) computes 256 output
+// channels x 256 tokens; wavefront (wf, wt) owns channels 128 wf .. +127 and
+// tokens 64 wt .. +63 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (channels
+// are the MFMA rows, tokens its columns, so each lane ends with runs of four
 // consecutive channels of one token).  The contracted dimension advances 32
 // at a time through a ring of four 32 KiB LDS stages, each holding the
 // 256 x 32 slices of W and X; row r's 16-byte chunk c sits at chunk
 // c ^ ((r >> 2) & 3) of its 64-byte row, so the 16 rows that one LDS cycle
 // serves of an operand read (16 lanes x 16 bytes over 64 banks) fall on
 // distinct banks.  Slices are copied with
-// global_load_lds_dwordx4 (16 rows x 64 bytes per instruction) three stages
-// ahead; one barrier per stage both publishes a stage and frees the oldest;
+// global_load_lds_dwordx4 (16 rows x 64 bytes per instruction; each
+// wavefront copies 32 rows of W and 32 of X per stage) three stages ahead; one barrier per stage both publishes a stage and frees the oldest;
 // operands are read from LDS one MFMA step ahead of their use.
 #include "vsa_internal.h"
 
@@ -49,26 +49,21 @@ struct GemmArgs {
     int tiles_n;         // n_out / 256 * 4
 };
 
-// Four 1 KiB direct-to-LDS copies: instruction i writes LDS bytes
-// slot + 1024 i + 16 lane from global base + voff[i] (per-lane offsets that
-// select row 16 i + lane / 4 and the swizzled 16-byte chunk of it).
-__device__ __forceinline__ void fetch4(uint32_t slot, const void* base, const uint32_t (&voff)[8]) {
-    asm volatile(
-        "s_mov_b32 m0, %[s]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v0], %[b]\n\t"
-        "s_add_u32 m0, %[s], 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v1], %[b]\n\t"
-        "s_add_u32 m0, %[s], 0x800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v2], %[b]\n\t"
-        "s_add_u32 m0, %[s], 0xc00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v3], %[b]"
-        :
-        : [s] "s"(slot), [b] "s"(base), [v0] "v"(voff[0]), [v1] "v"(voff[1]), [v2] "v"(voff[2]),
-          [v3] "v"(voff[3])
-        : "memory", "m0", "scc");
-}
-
 __device__ __forceinline__ void wait_vm(int n) {
-    if (n >= 16) __builtin_amdgcn_s_waitcnt(0x4F70);      // vmcnt(16)
-    else if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
+    if (n >= 8) __builtin_amdgcn_s_waitcnt(0x0F78);       // vmcnt(8)
+    else if (n >= 4) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
     else __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0)
     asm volatile("" ::: "memory");
+}
+
+// Two 1 KiB direct-to-LDS copies (slot, slot + 1024) from base + voff[0], voff[1].
+__device__ __forceinline__ void fetch2(uint32_t slot, const void* base, uint32_t v0, uint32_t v1) {
+    asm volatile(
+        "s_mov_b32 m0, %[s]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v0], %[b]\n\t"
+        "s_add_u32 m0, %[s], 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v1], %[b]"
+        :
+        : [s] "s"(slot), [b] "s"(base), [v0] "v"(v0), [v1] "v"(v1)
+        : "memory", "m0", "scc");
 }
 
 __device__ __forceinline__ void barrier() {
@@ -79,12 +74,12 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(256) void gemm_qkvg_kernel(GemmArgs a) {
+__global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
     extern __shared__ __align__(1024) unsigned char smem[];  // 4 stages x 32 KiB
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-    const int wf = wave & 1, wt = wave >> 1;
+    const int wf = wave & 1, wt = wave >> 1;  // 128 channels x 64 tokens per wave
 
     // Tile order: workgroups are dealt round-robin to the 8 XCDs; each XCD
     // walks its own share of the tiles channel-tile-major within a band of
@@ -113,61 +108,62 @@ __global__ __launch_bounds__(256) void gemm_qkvg_kernel(GemmArgs a) {
     // instructions (64 rows each, 16 per instruction): row 64 wave + 16 i +
     // lane / 4, global chunk (lane % 4) ^ ((row >> 2) & 3).  Token rows past
     // the end read the last token (valid memory; never stored).
-    uint32_t wo[8], xo[8];
+    uint32_t wo[2], xo[2];
     {
         const int rl = lane >> 2, ch = (lane & 3) ^ ((rl >> 2) & 3);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 64 * wave + 16 * i + rl;
+        for (int i = 0; i < 2; ++i) {
+            const int r = 32 * wave + 16 * i + rl;
             wo[i] = (uint32_t)((r * K + 8 * ch) * 2);
             const int64_t tr = t0 + r < a.tokens ? r : (int)(a.tokens - 1 - t0);
             xo[i] = (uint32_t)((tr * K + 8 * ch) * 2);
         }
-#pragma unroll
-        for (int i = 4; i < 8; ++i) wo[i] = xo[i] = 0;  // unused
     }
-    // 4 W and 4 X copies of 1 KiB (16 rows each) for stage buffer `buf`
+    // 2 W and 2 X copies of 1 KiB (16 rows each) for stage buffer `buf`
     auto fetch_stage = [&](int buf, int k0) {
         const uint32_t st = lds0 + (uint32_t)buf * kStageBytes;
-        fetch4(st + 4096u * wave, wbase + k0, wo);             // W rows 64 wave .. +63
-        fetch4(st + 16384u + 4096u * wave, xbase + k0, xo);    // X rows 64 wave .. +63
+        fetch2(st + 2048u * wave, wbase + k0, wo[0], wo[1]);           // W rows 32 wave .. +31
+        fetch2(st + 16384u + 2048u * wave, xbase + k0, xo[0], xo[1]);  // X rows 32 wave .. +31
     };
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     // operand read offsets inside a stage for MFMA step s (0, 1): rows
     // 32 i + lane % 32 of the wave's half, chunk (lane / 32) + 2 s swizzled
     const int orow = lane & 31, ohalf = lane >> 5;
-    uint32_t ow[2][4], ox[2][4];
+    uint32_t ow[2][4], ox[2][2];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const int c = ohalf + 2 * s2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int c = ohalf + 2 * s2;
             const int rw = 128 * wf + 32 * i + orow;
             ow[s2][i] = (uint32_t)(rw * 64 + 16 * (c ^ ((rw >> 2) & 3)));
-            const int rx = 128 * wt + 32 * i + orow;
-            ox[s2][i] = 16384u + (uint32_t)(rx * 64 + 16 * (c ^ ((rx >> 2) & 3)));
         }
-    auto read_ops = [&](bf16x8 (&wa)[4], bf16x8 (&xb)[4], int buf, int s2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int rx = 64 * wt + 32 * j + orow;
+            ox[s2][j] = 16384u + (uint32_t)(rx * 64 + 16 * (c ^ ((rx >> 2) & 3)));
+        }
+    }
+    auto read_ops = [&](bf16x8 (&wa)[4], bf16x8 (&xb)[2], int buf, int s2) {
         const uint32_t st = lds0 + (uint32_t)buf * kStageBytes;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            wa[i] = *(lds_bf16x8_ptr)(uintptr_t)(st + ow[s2][i]);
-            xb[i] = *(lds_bf16x8_ptr)(uintptr_t)(st + ox[s2][i]);
-        }
+        for (int i = 0; i < 4; ++i) wa[i] = *(lds_bf16x8_ptr)(uintptr_t)(st + ow[s2][i]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) xb[j] = *(lds_bf16x8_ptr)(uintptr_t)(st + ox[s2][j]);
     };
-    auto mfma_step = [&](const bf16x8 (&wa)[4], const bf16x8 (&xb)[4]) {
+    auto mfma_step = [&](const bf16x8 (&wa)[4], const bf16x8 (&xb)[2]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(wa[i], xb[j], acc[i][j]);
+            for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(wa[i], xb[j], acc[i][j]);
     };
 
     // Ring: stage kt lives in buffer kt % 4; each wave issues 8 copies per
@@ -175,11 +171,11 @@ __global__ __launch_bounds__(256) void gemm_qkvg_kernel(GemmArgs a) {
     const int KT = K / kBK;
     for (int p = 0; p < 3; ++p)
         if (p < KT) fetch_stage(p, p * kBK);
-    if (KT >= 3) wait_vm(16);
-    else if (KT == 2) wait_vm(8);
+    if (KT >= 3) wait_vm(8);
+    else if (KT == 2) wait_vm(4);
     else wait_vm(0);
     barrier();
-    bf16x8 wa0[4], xb0[4], wa1[4], xb1[4];
+    bf16x8 wa0[4], xb0[2], wa1[4], xb1[2];
     read_ops(wa0, xb0, 0, 0);
     // one stage: publish stage kt+1 (copies issued two iterations earlier)
     // and retire stage kt-1, whose buffer then takes stage kt+3; MFMA steps
@@ -202,8 +198,8 @@ __global__ __launch_bounds__(256) void gemm_qkvg_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     };
     int kt = 0;
-    for (; kt + 3 < KT; ++kt) stage(kt, 8, true, true);
-    if (kt + 2 < KT) stage(kt++, 8, true, false);
+    for (; kt + 3 < KT; ++kt) stage(kt, 4, true, true);
+    if (kt + 2 < KT) stage(kt++, 4, true, false);
     if (kt + 1 < KT) stage(kt++, 0, true, false);
     stage(kt, 0, false, false);
     barrier();  // every wave is done with the ring before it becomes staging
@@ -211,11 +207,11 @@ __global__ __launch_bounds__(256) void gemm_qkvg_kernel(GemmArgs a) {
     // ---- epilogue: bf16, staged through LDS as [token][channel], then
     // 16-byte stores along each token's row
     // lane l of block (i, j): token 32 j + l % 32, channels 32 i + 8 q + 4 (l / 32) + r
-    unsigned char* stg = smem + wave * 32768;  // 128 tokens x 128 channels x 2 B
+    unsigned char* stg = smem + wave * 16384;  // 64 tokens x 128 channels x 2 B
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
@@ -229,10 +225,10 @@ __global__ __launch_bounds__(256) void gemm_qkvg_kernel(GemmArgs a) {
     __syncthreads();
     uint16_t* obase = a.out[proj];
 #pragma unroll 4
-    for (int it = 0; it < 32; ++it) {
-        const int id = it * 64 + lane;       // 2048 chunks of 16 bytes
+    for (int it = 0; it < 16; ++it) {
+        const int id = it * 64 + lane;       // 1024 chunks of 16 bytes
         const int tok = id >> 4, chunk = id & 15;
-        const int64_t gt = t0 + 128 * wt + tok;
+        const int64_t gt = t0 + 64 * wt + tok;
         const uint4 v = *(const uint4*)(stg + tok * 256 + 16 * (chunk ^ (tok & 15)));
         if (gt < a.tokens)
             *(uint4*)(obase + gt * a.n_out + n0 + 128 * wf + 8 * chunk) = v;
@@ -260,7 +256,7 @@ hipError_t launch_project_qkvg(const uint16_t* x, const uint16_t* w, uint16_t* c
     a.n_out = n_out;
     a.tiles_n = 4 * (n_out / kBM);
     const int64_t tiles = ((tokens + kBT - 1) / kBT) * a.tiles_n;
-    hipLaunchKernelGGL(gemm_qkvg_kernel, dim3((unsigned)tiles), dim3(256), kStages * kStageBytes, stream, a);
+    hipLaunchKernelGGL(gemm_qkvg_kernel, dim3((unsigned)tiles), dim3(512), kStages * kStageBytes, stream, a);
     return hipGetLastError();
 }
 

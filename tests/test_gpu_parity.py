@@ -188,6 +188,30 @@ def test_long_rows_use_the_radix_select():
     G.assert_outputs_close(G.from_dev_bits(out)[rows], ref_out)
 
 
+@pytest.mark.slow
+def test_maximum_video_tiles():
+    """The largest video segment the library takes (16,384 tiles, 1,048,576
+    video tokens; k = 3,277): the radix select on one-row workgroups, 64-bit
+    offsets in every stage.  Every selection row and the coarse branch are
+    checked; outputs on sampled rows (a text row attends to all 1,048,704
+    keys)."""
+    h, s_t, s_v, s_a = 1, 64, 64 * 16384, 64
+    announce(f"maximum n_v: h={h} ({s_t},{s_v},{s_a}) k={bsv.vsa_topk_count(s_v, 0.2)}")
+    x = synth.vsa_inputs(18, h, s_t, s_v, s_a, threads=THREADS)
+    xd = G.inputs_to_dev(x)
+    out, sel, ws = G.run_forward(xd, s_t, s_v, s_a, 0.2)
+    ref = oracle.select_coarse(x["q"], x["k"], x["v"], s_t, s_v, s_a, 0.2, threads=THREADS)
+    got_sel = sel.cpu().numpy()
+    assert ref["k"] == 3277
+    G.check_selection(got_sel, ref)
+    w = G.read_workspace(ws, h, s_t, s_v, s_a)
+    np.testing.assert_allclose(w["coarse"], ref["coarse"], rtol=2e-5, atol=2e-7)
+    rows = G.sample_rows(s_t, s_v, s_a, n_video_tiles=3, per_tile=(0, 63))
+    _, ref_out = oracle.fine(x["q"], x["k"], x["v"], x["gate"], s_t, s_v, s_a, got_sel,
+                             ref["coarse"], rows, threads=THREADS)
+    G.assert_outputs_close(G.from_dev_bits(out)[rows], ref_out)
+
+
 def test_designed_ranking():
     announce("designed ranking")
     h, s_t, n_v = 1, 64, 15
