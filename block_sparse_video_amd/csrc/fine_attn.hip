@@ -68,7 +68,9 @@ struct FineArgs {
 // within the last-level cache, and the ~1,000 concurrently resident units
 // of one head start together and sweep their ascending key lists at the same
 // pace.  The dense units (N key tiles each, ~4.5x a video unit) then start
-// together and sweep every tile of their heads in step.
+// together and sweep every tile of their heads in step; each XCD takes a
+// contiguous head-major range of them, so all dense units of a head share
+// one XCD's L2 instead of each of the eight fetching the head.
 __device__ __forceinline__ void unit_of(int b, int H, int n_t, int n_v, int n_a, int& h, int& j) {
     const int n_h = n_t + n_a;
     const int V = H * n_v;
@@ -76,9 +78,20 @@ __device__ __forceinline__ void unit_of(int b, int H, int n_t, int n_v, int n_a,
         h = b / n_v;
         j = n_t + (b - h * n_v);
     } else {
+        // dense units: each XCD (block index mod 8) takes a contiguous,
+        // head-major range of them, so the units of one head share one L2
+        const int D = H * n_h;
         const int c = b - V;
-        h = c / n_h;
-        const int p = c - h * n_h;
+        const int g = b & 7;
+        const int f = ((g - V) % 8 + 8) % 8;  // first c with (c + V) mod 8 == g
+        int start = 0;
+        for (int q = 0; q < g; ++q) {
+            const int fq = ((q - V) % 8 + 8) % 8;
+            start += fq < D ? (D - fq + 7) / 8 : 0;
+        }
+        const int item = start + (c - f) / 8;
+        h = item / n_h;
+        const int p = item - h * n_h;
         j = p < n_t ? p : n_v + p;
     }
 }
