@@ -242,3 +242,38 @@ def test_full_size_10s_56h_sampled():
     _, ref_out = oracle.fine(x["q"], x["k"], x["v"], np.zeros_like(x["q"]), s_t, s_v, s_a, got,
                              np.zeros((h, n_v, D)), rows, threads=THREADS)
     G.assert_outputs_close(G.from_dev_bits(out)[rows], ref_out)
+
+
+def test_subblock_graph_capture_replays():
+    """vsa_forward_subblock with a caller workspace records into a HIP graph;
+    replays with new inputs match eager calls bit for bit."""
+    announce("subblock graph capture: h=2 tiles=(1,30,1)")
+    s_t, s_v, s_a = 64, 64 * 30, 64
+    h = 2
+    xs = [G.inputs_to_dev({n: a for n, a in synth.vsa_inputs(40 + i, h, s_t, s_v, s_a).items()
+                           if n != "gate"}) for i in range(2)]
+    static = {n: t.clone() for n, t in xs[0].items()}
+    out, sel, ws = bsv.alloc_subblock_outputs(h, s_t, s_v, s_a, 0.75)
+    call = lambda d, o, s_, w: bsv.vsa_forward_subblock(d["q"], d["k"], d["v"], s_t, s_v, s_a,
+                                                        0.75, o, s_, w)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(static, out, sel, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(static, out, sel, ws)
+    torch.cuda.synchronize()
+    for rep in (0, 1, 0):
+        for n in static:
+            static[n].copy_(xs[rep][n])
+        graph.replay()
+        torch.cuda.synchronize()
+        got_o, got_s = out.clone(), sel.clone()
+        e_out, e_sel, e_ws = bsv.alloc_subblock_outputs(h, s_t, s_v, s_a, 0.75)
+        call(xs[rep], e_out, e_sel, e_ws)
+        torch.cuda.synchronize()
+        assert torch.equal(got_o.view(torch.int16), e_out.view(torch.int16)), rep
+        assert torch.equal(got_s, e_sel), rep
