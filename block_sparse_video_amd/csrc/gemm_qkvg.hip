@@ -13,15 +13,16 @@
 // channels x 256 tokens; wavefront (wf, wt) owns channels 128 wf .. +127 and
 // tokens 64 wt .. +63 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (channels
 // are the MFMA rows, tokens its columns, so each lane ends with runs of four
-// consecutive channels of one token).  The contracted dimension advances 32
-// at a time through a ring of four 32 KiB LDS stages, each holding the
-// 256 x 32 slices of W and X; row r's 16-byte chunk c sits at chunk
-// c ^ ((r >> 2) & 3) of its 64-byte row, so the 16 rows that one LDS cycle
+// consecutive channels of one token).  The contracted dimension advances 64
+// at a time through two 64 KiB LDS stages (double buffering), each holding
+// the 256 x 64 slices of W and X; row r's 16-byte chunk c sits at chunk
+// c ^ ((r >> 1) & 7) of its 128-byte row, so the 16 rows that one LDS cycle
 // serves of an operand read (16 lanes x 16 bytes over 64 banks) fall on
-// distinct banks.  Slices are copied with
-// global_load_lds_dwordx4 (16 rows x 64 bytes per instruction; each
-// wavefront copies 32 rows of W and 32 of X per stage) three stages ahead; one barrier per stage both publishes a stage and frees the oldest;
-// operands are read from LDS one MFMA step ahead of their use.
+// distinct banks.  Slices are copied with global_load_lds_dwordx4 (8 rows x
+// 128 bytes per instruction; each wavefront copies 32 rows of W and 32 of X
+// per stage) one stage ahead; one barrier per stage both publishes the next
+// stage and frees the current buffer for the stage after it; operands are
+// read from LDS one MFMA step ahead of their use.
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -36,8 +37,8 @@ typedef __attribute__((address_space(3))) const bf16x8* lds_bf16x8_ptr;
 
 constexpr int kBM = 256;       // channels per workgroup
 constexpr int kBT = 256;       // tokens per workgroup
-constexpr int kBK = 32;        // contracted slice per stage
-constexpr int kStages = 4;     // LDS ring depth
+constexpr int kBK = 64;        // contracted slice per stage
+constexpr int kStages = 2;     // LDS ring depth
 constexpr int kStageBytes = (kBM + kBT) * kBK * 2;  // 32 KiB
 
 struct GemmArgs {
@@ -57,12 +58,15 @@ __device__ __forceinline__ void wait_vm(int n) {
 }
 
 // Two 1 KiB direct-to-LDS copies (slot, slot + 1024) from base + voff[0], voff[1].
-__device__ __forceinline__ void fetch2(uint32_t slot, const void* base, uint32_t v0, uint32_t v1) {
+__device__ __forceinline__ void fetch4(uint32_t slot, const void* base, const uint32_t (&v)[4]) {
     asm volatile(
         "s_mov_b32 m0, %[s]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v0], %[b]\n\t"
-        "s_add_u32 m0, %[s], 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v1], %[b]"
+        "s_add_u32 m0, %[s], 0x400\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v1], %[b]\n\t"
+        "s_add_u32 m0, %[s], 0x800\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v2], %[b]\n\t"
+        "s_add_u32 m0, %[s], 0xc00\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v3], %[b]"
         :
-        : [s] "s"(slot), [b] "s"(base), [v0] "v"(v0), [v1] "v"(v1)
+        : [s] "s"(slot), [b] "s"(base), [v0] "v"(v[0]), [v1] "v"(v[1]), [v2] "v"(v[2]),
+          [v3] "v"(v[3])
         : "memory", "m0", "scc");
 }
 
@@ -75,7 +79,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 }
 
 __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
-    extern __shared__ __align__(1024) unsigned char smem[];  // 4 stages x 32 KiB
+    extern __shared__ __align__(1024) unsigned char smem[];  // 2 stages x 64 KiB
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr_t)smem;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -83,14 +87,14 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
 
     // Tile order: workgroups are dealt round-robin to the 8 XCDs; each XCD
     // walks its own share of the tiles channel-tile-major within a band of
-    // 8 token tiles, so the tiles running together on one XCD share their
+    // 4 token tiles, so the tiles running together on one XCD share their
     // W and X slices in its L2.
     const int tiles_t = (int)((a.tokens + kBT - 1) / kBT);
     const int nb = gridDim.x;  // = tiles_t * tiles_n
     const int b = blockIdx.x;
     const int x8 = b & 7, q8 = nb >> 3, r8 = nb & 7;
     const int lin = x8 * q8 + (x8 < r8 ? x8 : r8) + (b >> 3);  // XCD x8: a contiguous range
-    constexpr int kBand = 8;
+    constexpr int kBand = 4;
     const int band = lin / (kBand * a.tiles_n);
     const int in_band = lin - band * kBand * a.tiles_n;
     const int band_t = min(kBand, tiles_t - band * kBand);
@@ -105,25 +109,26 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
     const uint16_t* xbase = a.x + t0 * K;
 
     // Per-lane byte offsets of this wave's 4 W-row and 4 X-row copy
-    // instructions (64 rows each, 16 per instruction): row 64 wave + 16 i +
-    // lane / 4, global chunk (lane % 4) ^ ((row >> 2) & 3).  Token rows past
+    // instructions (32 rows each, 8 per instruction): row 32 wave + 8 i +
+    // lane / 8, global chunk (lane % 8) ^ ((row >> 1) & 7).  Token rows past
     // the end read the last token (valid memory; never stored).
-    uint32_t wo[2], xo[2];
+    uint32_t wo[4], xo[4];
     {
-        const int rl = lane >> 2, ch = (lane & 3) ^ ((rl >> 2) & 3);
+        const int rl = lane >> 3;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = 32 * wave + 16 * i + rl;
+        for (int i = 0; i < 4; ++i) {
+            const int r = 32 * wave + 8 * i + rl;
+            const int ch = (lane & 7) ^ ((r >> 1) & 7);
             wo[i] = (uint32_t)((r * K + 8 * ch) * 2);
             const int64_t tr = t0 + r < a.tokens ? r : (int)(a.tokens - 1 - t0);
             xo[i] = (uint32_t)((tr * K + 8 * ch) * 2);
         }
     }
-    // 2 W and 2 X copies of 1 KiB (16 rows each) for stage buffer `buf`
+    // 4 W and 4 X copies of 1 KiB (8 rows of 128 bytes each) for stage buffer `buf`
     auto fetch_stage = [&](int buf, int k0) {
         const uint32_t st = lds0 + (uint32_t)buf * kStageBytes;
-        fetch2(st + 2048u * wave, wbase + k0, wo[0], wo[1]);           // W rows 32 wave .. +31
-        fetch2(st + 16384u + 2048u * wave, xbase + k0, xo[0], xo[1]);  // X rows 32 wave .. +31
+        fetch4(st + 4096u * wave, wbase + k0, wo);           // W rows 32 wave .. +31
+        fetch4(st + 32768u + 4096u * wave, xbase + k0, xo);  // X rows 32 wave .. +31
     };
 
     f32x16 acc[4][2];
@@ -137,19 +142,19 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
     // operand read offsets inside a stage for MFMA step s (0, 1): rows
     // 32 i + lane % 32 of the wave's half, chunk (lane / 32) + 2 s swizzled
     const int orow = lane & 31, ohalf = lane >> 5;
-    uint32_t ow[2][4], ox[2][2];
+    uint32_t ow[4][4], ox[4][2];
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    for (int s2 = 0; s2 < 4; ++s2) {
         const int c = ohalf + 2 * s2;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int rw = 128 * wf + 32 * i + orow;
-            ow[s2][i] = (uint32_t)(rw * 64 + 16 * (c ^ ((rw >> 2) & 3)));
+            ow[s2][i] = (uint32_t)(rw * 128 + 16 * (c ^ ((rw >> 1) & 7)));
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int rx = 64 * wt + 32 * j + orow;
-            ox[s2][j] = 16384u + (uint32_t)(rx * 64 + 16 * (c ^ ((rx >> 2) & 3)));
+            ox[s2][j] = 32768u + (uint32_t)(rx * 128 + 16 * (c ^ ((rx >> 1) & 7)));
         }
     }
     auto read_ops = [&](bf16x8 (&wa)[4], bf16x8 (&xb)[2], int buf, int s2) {
@@ -166,42 +171,33 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
             for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(wa[i], xb[j], acc[i][j]);
     };
 
-    // Ring: stage kt lives in buffer kt % 4; each wave issues 8 copies per
-    // stage.  Prologue: stages 0, 1, 2 in flight; publish stage 0.
+    // Ring: stage kt lives in buffer kt % 2.  Each stage: MFMA steps 0..3,
+    // each with the next step's operands read beside it; before the last
+    // step, one barrier publishes stage kt+1 and frees buffer kt % 2, which
+    // then takes stage kt+2.
     const int KT = K / kBK;
-    for (int p = 0; p < 3; ++p)
-        if (p < KT) fetch_stage(p, p * kBK);
-    if (KT >= 3) wait_vm(8);
-    else if (KT == 2) wait_vm(4);
-    else wait_vm(0);
+    fetch_stage(0, 0);
+    if (KT > 1) fetch_stage(1, kBK);
+    wait_vm(KT > 1 ? 8 : 0);
     barrier();
     bf16x8 wa0[4], xb0[2], wa1[4], xb1[2];
     read_ops(wa0, xb0, 0, 0);
-    // one stage: publish stage kt+1 (copies issued two iterations earlier)
-    // and retire stage kt-1, whose buffer then takes stage kt+3; MFMA steps
-    // 0 and 1 of stage kt, each with the next step's operands read beside it
-    auto stage = [&](int kt, int wait_n, bool publish, bool refill) {
-        if (publish) {
-            wait_vm(wait_n);
-            barrier();
-            if (refill) fetch_stage((kt + 3) & 3, (kt + 3) * kBK);
-        }
-        // the scheduling fences keep each step's LDS reads a full MFMA step
-        // ahead of their use instead of next to it
-        read_ops(wa1, xb1, kt & 3, 1);
-        __builtin_amdgcn_sched_barrier(0);
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        read_ops(wa1, xb1, buf, 1);
         mfma_step(wa0, xb0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (publish) read_ops(wa0, xb0, (kt + 1) & 3, 0);
-        __builtin_amdgcn_sched_barrier(0);
+        read_ops(wa0, xb0, buf, 2);
         mfma_step(wa1, xb1);
-        __builtin_amdgcn_sched_barrier(0);
-    };
-    int kt = 0;
-    for (; kt + 3 < KT; ++kt) stage(kt, 4, true, true);
-    if (kt + 2 < KT) stage(kt++, 4, true, false);
-    if (kt + 1 < KT) stage(kt++, 0, true, false);
-    stage(kt, 0, false, false);
+        read_ops(wa1, xb1, buf, 3);
+        mfma_step(wa0, xb0);
+        if (kt + 1 < KT) {
+            wait_vm(0);
+            barrier();
+            if (kt + 2 < KT) fetch_stage(buf, (kt + 2) * kBK);
+            read_ops(wa0, xb0, buf ^ 1, 0);
+        }
+        mfma_step(wa1, xb1);
+    }
     barrier();  // every wave is done with the ring before it becomes staging
 
     // ---- epilogue: bf16, staged through LDS as [token][channel], then
