@@ -51,11 +51,22 @@ def tile_pairs(h, s_t, s_v, s_a, k):
 
 
 def pool_pack_bytes(h, s_t, s_v, s_a):
-    """Algorithmic HBM bytes of stage 1: read Q, K video rows and all V rows,
-    write pooled statistics (8 + 4 + 4 bytes per element) and the V pack."""
+    """Algorithmic HBM bytes of stage 1: read the Q video rows and every K
+    and V row, write the K and V packs and the pooled statistics (8 + 4 + 4
+    bytes per element of Q, K, V means)."""
     s = s_t + s_v + s_a
     n_v = s_v // TILE
-    return 2 * s_v * h * D * 2 + s * h * D * 2 + h * n_v * D * 16 + s * h * D * 2
+    return s_v * h * D * 2 + 2 * s * h * D * 2 + 2 * s * h * D * 2 + h * n_v * D * 16
+
+
+def select_coarse_work(h, s_v, k):
+    """Algorithmic work of stage 2: float64 tile scores (2 n_v^2 128 FLOP per
+    head) and the coarse product (the same count), and its HBM bytes (pooled
+    statistics in, selection and coarse vectors out)."""
+    n_v = s_v // TILE
+    flop = 2 * 2.0 * h * n_v * n_v * D
+    nbytes = h * n_v * D * (8 + 4 + 4) + h * n_v * k * 4 + h * n_v * D * 4
+    return flop, nbytes
 
 
 def source_hash(path):
@@ -406,6 +417,9 @@ def main():
             "pool_pack_ms": r["stage_ms"][0],
             "pool_pack_GBs": pool_pack_bytes(h, s_t, s_v, s_a) / (r["stage_ms"][0] * 1e-3) / 1e9,
             "select_coarse_ms": r["stage_ms"][1],
+            "select_coarse_fp64_tflops": select_coarse_work(h, s_v, kk)[0] / (r["stage_ms"][1] * 1e-3) / 1e12,
+            "select_coarse_fp64_frac_of_78.6": select_coarse_work(h, s_v, kk)[0] / (r["stage_ms"][1] * 1e-3) / 1e12 / PEAK_FP64_TFLOPS,
+            "select_coarse_GBs": select_coarse_work(h, s_v, kk)[1] / (r["stage_ms"][1] * 1e-3) / 1e9,
             "fine_attn_ms": fine_ms,
             "forward_entry_ms": r["forward_ms"],
             "forward_entry_ms_median_min_p90": [r["forward_stats"]["median"],
