@@ -235,14 +235,10 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
 
 hipError_t launch_project_qkvg(const uint16_t* x, const uint16_t* w, uint16_t* const out[4],
                                int64_t tokens, int hidden, int n_out, hipStream_t stream) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)gemm_qkvg_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           kStages * kStageBytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static std::atomic<size_t> lds_allowed[kMaxDevices];
+    hipError_t e = ensure_dynamic_lds((const void*)gemm_qkvg_kernel, lds_allowed,
+                                      (size_t)kStages * kStageBytes);
+    if (e != hipSuccess) return e;
     GemmArgs a;
     a.x = x;
     a.w = w;

@@ -208,13 +208,9 @@ template <int R, int NS>
 hipError_t launch_r(const Shape& s, int32_t* sel, uint8_t* ws, const Layout& L, hipStream_t stream,
                     int ldw, size_t lds) {
     // Raise the kernel's dynamic-LDS limit when a larger row pitch needs it.
-    static std::atomic<size_t> lds_allowed{0};
-    if (lds > lds_allowed.load()) {
-        hipError_t e = hipFuncSetAttribute((const void*)select_coarse_kernel<R, NS>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        lds_allowed.store(lds);
-    }
+    static std::atomic<size_t> lds_allowed[kMaxDevices];
+    hipError_t e = ensure_dynamic_lds((const void*)select_coarse_kernel<R, NS>, lds_allowed, lds);
+    if (e != hipSuccess) return e;
     dim3 grid((s.n_v + R - 1) / R, s.H);
     const float alpha = (float)(1.0 / 11.313708498984761);  // 1/sqrt(128)
     hipLaunchKernelGGL((select_coarse_kernel<R, NS>), grid, dim3(256), lds, stream,

@@ -228,13 +228,9 @@ hipError_t launch_route(const Shape& s, int32_t* sel, const uint8_t* ws, const L
     const int n_c = (s.n_v + 3) / 4;
     const int ldw = (s.n_v + 3) & ~3;
     const size_t lds = (size_t)4 * RT * ldw * sizeof(double);
-    static std::atomic<size_t> lds_allowed{0};
-    if (lds > lds_allowed.load()) {
-        hipError_t e = hipFuncSetAttribute((const void*)subblock_route_kernel<RT, NS>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        lds_allowed.store(lds);
-    }
+    static std::atomic<size_t> lds_allowed[kMaxDevices];
+    hipError_t e = ensure_dynamic_lds((const void*)subblock_route_kernel<RT, NS>, lds_allowed, lds);
+    if (e != hipSuccess) return e;
     const int64_t blocks = (int64_t)s.H * ((n_c + RT - 1) / RT);
     hipLaunchKernelGGL((subblock_route_kernel<RT, NS>), dim3((unsigned)blocks), dim3(512), lds,
                        stream, (const float*)(ws + L.qsub), (const float*)(ws + L.ksub), s.H,

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <atomic>
+
 namespace vsa {
 
 constexpr int kD = 128;   // head dimension
@@ -74,6 +76,27 @@ inline Layout make_layout(const Shape& s, bool subblock = false) {
     L.ksub = off;   off = align_up(off + sub);
     L.total = off;
     return L;
+}
+
+// Devices a process may use with this library (the host entry points
+// reject device ordinals at or past it).
+constexpr int kMaxDevices = 64;
+
+// Raise `kernel`'s dynamic-LDS limit to `bytes` on the current device the
+// first time a launch there needs it; `allowed` keeps the limit set so far per
+// device (concurrent first calls only repeat the same attribute call).
+inline hipError_t ensure_dynamic_lds(const void* kernel, std::atomic<size_t>* allowed,
+                                     size_t bytes) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    if (bytes > allowed[dev].load()) {
+        e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+        if (e != hipSuccess) return e;
+        allowed[dev].store(bytes);
+    }
+    return hipSuccess;
 }
 
 // ---- launchers (each enqueues on `stream`, returns the launch status) ----
