@@ -229,6 +229,36 @@ def test_designed_ranking():
     assert np.array_equal(sel[0, 0], [0, 1, 2])
 
 
+def test_late_large_scores_recompute():
+    """The fine kernel's softmax reference is the column max of the first
+    half-tile it meets; a later key tile scoring far above it makes the
+    denominator pass 2^100 and the unit is recomputed with a raised
+    reference.  Head 0: the excess is ~110 (log2 units), a finite sum past
+    2^100 (one extra pass).  Head 1: ~330, where the first sums overflow
+    to inf (two extra passes).  Text keys are 0, so every list starts at
+    score 0."""
+    announce("late large scores: h=2 tiles=(1,16,1)")
+    h, s_t, n_v, s_a = 2, 64, 16, 64
+    s_v = n_v * T
+    x = synth.vsa_inputs(17, h, s_t, s_v, s_a)
+    q = G.widen(x["q"]).astype(np.float32)
+    k = G.widen(x["k"]).astype(np.float32)
+    w_star = 9
+    for hh, c in ((0, 2.6), (1, 4.5)):
+        q[:, hh] = c
+        k[:s_t, hh] = 0.0
+        k[s_t + w_star * T: s_t + (w_star + 1) * T, hh] = c
+    x["q"], x["k"] = synth.f32_to_bf16_bits(q), synth.f32_to_bf16_bits(k)
+    # the inputs do reach the recompute condition (host arithmetic)
+    c2 = np.log2(np.e) / np.sqrt(D)
+    qw, kw = G.widen(x["q"]), G.widen(x["k"])
+    top = [float(qw[0, hh] @ kw[s_t + w_star * T, hh]) * c2 for hh in range(h)]
+    assert 100 < top[0] < 120 and top[1] > 300, top
+    ref, e, *_ = full_check(x, s_t, s_v, s_a, 0.2, exempt_ok=False)
+    assert np.all(ref["sel"][:, :, -1] >= w_star) and np.all(np.any(ref["sel"] == w_star, axis=-1))
+    print(e)
+
+
 def test_fine_stage_on_oracle_selection():
     """The fine stage honours the index sets it is given: run it on the
     oracle's own selection (and on a shifted one) and compare."""
