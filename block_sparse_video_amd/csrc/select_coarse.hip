@@ -182,10 +182,25 @@ __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __rest
     const double* prow[RH];
 #pragma unroll
     for (int i = 0; i < RH; ++i) prow[i] = sc + min(half * RH + i, R - 1) * ldw;
+    // pooled V values of the next group of 32 columns are requested while
+    // the current group is multiplied
+    float vn[32];
+    auto load_group = [&](int w0) {
+        if (w0 + 32 <= n_v) {
+            const float* p = vb + (int64_t)w0 * kD;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) vn[i] = p[i * kD];
+        } else {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) vn[i] = vb[(int64_t)min(w0 + i, n_v - 1) * kD];
+        }
+    };
+    load_group(0);
     for (int w0 = 0; w0 < n_v; w0 += 32) {
         float vr[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) vr[i] = vb[(int64_t)min(w0 + i, n_v - 1) * kD];
+        for (int i = 0; i < 32; ++i) vr[i] = vn[i];
+        if (w0 + 32 < n_v) load_group(w0 + 32);
 #pragma unroll
         for (int i = 0; i < 32; i += 2) {
 #pragma unroll
