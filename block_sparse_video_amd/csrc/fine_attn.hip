@@ -61,22 +61,43 @@ struct FineArgs {
     float scale_log2;   // log2(e) / sqrt(128)
 };
 
-// blockIdx -> (head, query tile).  All video units come first, head-major,
-// then all dense text/audio units.  Workgroups are dealt round-robin to the 8
-// XCDs, so during the video phase every XCD works on the same one or two
-// heads: the K/V tiles in flight (37 MB per head at the 10 s shape) stay
-// within the last-level cache, and the ~1,000 concurrently resident units
-// of one head start together and sweep their ascending key lists at the same
-// pace.  The dense units (N key tiles each, ~4.5x a video unit) then start
-// together and sweep every tile of their heads in step; each XCD takes a
-// contiguous head-major range of them, so all dense units of a head share
-// one XCD's L2 instead of each of the eight fetching the head.
+// blockIdx -> (head, query tile).  All video units come first, then all
+// dense text/audio units.  Workgroups are dealt round-robin to the 8 XCDs.
+// With an even head count, XCDs 0-3 walk the video units of the even heads
+// and XCDs 4-7 those of the odd heads, each group head-major: two heads are
+// in flight at a time, each on four XCDs, so each head's K/V tiles (37 MB at
+// the 10 s shape) are pulled into four L2s instead of eight while both stay
+// within the last-level cache; the ~1,000 concurrently resident units of a
+// head start together and sweep their ascending key lists at the same pace.
+// The dense units (N key tiles each, ~4.5x a video unit) then start together
+// and sweep every tile of their heads in step; each XCD takes a contiguous
+// head-major range of them, so all dense units of a head share one L2.
 __device__ __forceinline__ void unit_of(int b, int H, int n_t, int n_v, int n_a, int& h, int& j) {
     const int n_h = n_t + n_a;
     const int V = H * n_v;
     if (b < V) {
-        h = b / n_v;
-        j = n_t + (b - h * n_v);
+        if ((H & 1) == 0) {
+            // blocks in full rounds of 8 deal 4 units to each head group;
+            // the last V mod 8 blocks (an even count) take the rest, half
+            // per group
+            const int V8 = V & ~7;
+            int gp, ug;  // head group (parity) and unit index within it
+            if (b < V8) {
+                const int x = b & 7;
+                gp = x >> 2;
+                ug = 4 * (b >> 3) + (x & 3);
+            } else {
+                const int t = b - V8, r = (V - V8) >> 1;
+                gp = t / r;
+                ug = 4 * (V >> 3) + (t - gp * r);
+            }
+            const int hh = ug / n_v;
+            h = 2 * hh + gp;
+            j = n_t + (ug - hh * n_v);
+        } else {
+            h = b / n_v;
+            j = n_t + (b - h * n_v);
+        }
     } else {
         // dense units: each XCD (block index mod 8) takes a contiguous,
         // head-major range of them, so the units of one head share one L2
