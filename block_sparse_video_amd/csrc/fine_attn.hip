@@ -492,6 +492,22 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
     }
 
     // ---- epilogue: normalise, stage through LDS, add sigmoid(G) * coarse ----
+    // Lane l writes dims 8(l%16) .. +7 of rows l/16 + 4i, i < 16.  The gate
+    // rows (never read before, so they come from HBM) and the lane's eight
+    // coarse values are all requested here, before the staging, so their
+    // latency is paid once per unit rather than once per group of rows.
+    const bool gated = video && a.gate;
+    const int c16 = lane & 15;
+    uint4 gw[16];
+    float4 cv0, cv1;
+    if (gated) {
+        const uint16_t* gp = a.gate + ((int64_t)j * kT + (lane >> 4)) * rs + (int64_t)h * kD + 8 * c16;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) gw[i] = *(const uint4*)(gp + 4 * i * rs);
+        const float* cp = a.coarse + ((int64_t)h * a.n_v + u) * kD + 8 * c16;
+        cv0 = *(const float4*)cp;
+        cv1 = *(const float4*)(cp + 4);
+    }
     float* ost = (float*)lds;  // [64 queries][128 dims], 16-byte chunks swizzled by row
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -509,11 +525,9 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
             }
     }
     __syncthreads();
-    const float* cp = a.coarse + ((int64_t)h * a.n_v + (video ? u : 0)) * kD;
-#pragma unroll 4
+#pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const int id = lane + kThreads * i;
-        const int row = id >> 4, c = id & 15;
+        const int row = (lane >> 4) + 4 * i, c = c16;
         const float4 x0 = *(const float4*)(ost + row * kD + 4 * ((2 * c) ^ (row & 15)));
         const float4 x1 = *(const float4*)(ost + row * kD + 4 * ((2 * c + 1) ^ (row & 15)));
         f32x8 y = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -521,12 +535,9 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         if (row >= nq) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) y[e] = 0.0f;
-        } else if (video && a.gate) {
-            const uint4 gw = *(const uint4*)(a.gate + grow * rs + (int64_t)h * kD + 8 * c);
-            const float4 c0 = *(const float4*)(cp + 8 * c);
-            const float4 c1 = *(const float4*)(cp + 8 * c + 4);
-            const uint32_t gwv[4] = {gw.x, gw.y, gw.z, gw.w};
-            const float cv[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        } else if (gated) {
+            const uint32_t gwv[4] = {gw[i].x, gw[i].y, gw[i].z, gw[i].w};
+            const float cv[8] = {cv0.x, cv0.y, cv0.z, cv0.w, cv1.x, cv1.y, cv1.z, cv1.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 y[2 * e] += sigmoidf(__uint_as_float(gwv[e] << 16)) * cv[2 * e];
