@@ -12,6 +12,8 @@
 //
 // One wavefront computes one work unit (head h, query tile j): 64 query rows
 // against every key tile of the unit's list, walked as half-tiles of 32 keys.
+// The kernel is persistent: each single-wavefront workgroup takes units from
+// per-XCD work queues (counters in the workspace) until every queue is empty.
 // Every K/V element a unit needs is used by that wavefront only, so the
 // wavefront streams its operands into a private 40 KiB LDS ring (three K
 // slots, two V slots) with global_load_lds_dwordx4 and needs no barriers.
@@ -45,6 +47,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kThreads = 64;
+// s_getreg_b32 operand for HW_REG_XCC_ID (register 20, bits 0..31): the XCD
+// the wavefront runs on, in bits 0..3
+constexpr int kHwRegXccId = (31 << 11) | 20;
 constexpr int kHalfElems = 32 * kD;  // bf16 elements per packed half-tile (8 KiB)
 constexpr int kTileElems = 2 * kHalfElems;
 
@@ -56,65 +61,90 @@ struct FineArgs {
     const int32_t* sel;
     const float* coarse;
     uint16_t* out;
+    uint32_t* sched;    // kQueues work-queue counters, 32 words apart, zero at launch
     int H, n_t, n_v, n_a, N, kk;
     int last_valid[3];  // token rows in the last text / video / audio tile (64 when full)
     float scale_log2;   // log2(e) / sqrt(128)
 };
 
-// blockIdx -> (head, query tile).  All video units come first, then all
-// dense text/audio units.  Workgroups are dealt round-robin to the 8 XCDs.
-// With an even head count, XCDs 0-3 walk the video units of the even heads
-// and XCDs 4-7 those of the odd heads, each group head-major: two heads are
-// in flight at a time, each on four XCDs, so each head's K/V tiles (37 MB at
-// the 10 s shape) are pulled into four L2s instead of eight while both stay
-// within the last-level cache; the ~1,000 concurrently resident units of a
-// head start together and sweep their ascending key lists at the same pace.
-// The dense units (N key tiles each, ~4.5x a video unit) then start together
-// and sweep every tile of their heads in step; each XCD takes a contiguous
-// head-major range of them, so all dense units of a head share one L2.
-__device__ __forceinline__ void unit_of(int b, int H, int n_t, int n_v, int n_a, int& h, int& j) {
+// Work queues.  The kernel is persistent: one workgroup per wavefront slot,
+// each taking units (head h, query tile j) from kQueues queues until all are
+// empty.  Queue x is meant for XCD x and holds, in this order,
+//  - video units: with an even head count, XCDs 0-3 take the even heads' and
+//    XCDs 4-7 the odd heads', each group in head-major order dealt
+//    round-robin to its four XCDs.  Two heads are then in flight at a time,
+//    each pulled into four L2s instead of eight while both stay within the
+//    last-level cache, and the resident units of a head start together and
+//    sweep their ascending key lists at the same pace.  With an odd head
+//    count the video units are dealt round-robin to all eight queues;
+//  - then a contiguous, head-major 1/8 share of the dense (text/audio query)
+//    units (N key tiles each, ~4.5x a video unit), so the dense units of one
+//    head share one L2.  They start together once the video units are done
+//    and sweep every tile of their heads in step.  (Dense units first leaves
+//    no long units for the end, but measured 15-20% slower: the video units
+//    then start unevenly and lose their lockstep.)
+__device__ __forceinline__ int dense_begin(int D, int x) { return (int)(((int64_t)D * x) / kQueues); }
+
+__device__ __forceinline__ int video_count(int H, int n_v, int x) {
+    if ((H & 1) == 0) {
+        const int vg = (H >> 1) * n_v, m = x & 3;
+        return vg > m ? (vg - m + 3) / 4 : 0;
+    }
+    const int v = H * n_v;
+    return v > x ? (v - x + kQueues - 1) / kQueues : 0;
+}
+
+// Unit i of queue x -> (h, j).
+__device__ __forceinline__ void queue_unit(int H, int n_t, int n_v, int n_a, int x, int i, int& h,
+                                           int& j) {
     const int n_h = n_t + n_a;
-    const int V = H * n_v;
-    if (b < V) {
-        if ((H & 1) == 0) {
-            // blocks in full rounds of 8 deal 4 units to each head group;
-            // the last V mod 8 blocks (an even count) take the rest, half
-            // per group
-            const int V8 = V & ~7;
-            int gp, ug;  // head group (parity) and unit index within it
-            if (b < V8) {
-                const int x = b & 7;
-                gp = x >> 2;
-                ug = 4 * (b >> 3) + (x & 3);
-            } else {
-                const int t = b - V8, r = (V - V8) >> 1;
-                gp = t / r;
-                ug = 4 * (V >> 3) + (t - gp * r);
-            }
-            const int hh = ug / n_v;
-            h = 2 * hh + gp;
-            j = n_t + (ug - hh * n_v);
-        } else {
-            h = b / n_v;
-            j = n_t + (b - h * n_v);
-        }
-    } else {
-        // dense units: each XCD (block index mod 8) takes a contiguous,
-        // head-major range of them, so the units of one head share one L2
-        const int D = H * n_h;
-        const int c = b - V;
-        const int g = b & 7;
-        const int f = ((g - V) % 8 + 8) % 8;  // first c with (c + V) mod 8 == g
-        int start = 0;
-        for (int q = 0; q < g; ++q) {
-            const int fq = ((q - V) % 8 + 8) % 8;
-            start += fq < D ? (D - fq + 7) / 8 : 0;
-        }
-        const int item = start + (c - f) / 8;
+    const int D = H * n_h;
+    const int d0 = dense_begin(D, x);
+    const int nvx = video_count(H, n_v, x);
+    const bool dense = i >= nvx;
+    const int r = dense ? i - nvx : i;
+    if (dense) {
+        const int item = d0 + r;
         h = item / n_h;
         const int p = item - h * n_h;
         j = p < n_t ? p : n_v + p;
+    } else if ((H & 1) == 0) {
+        const int ug = (x & 3) + 4 * r;
+        const int hh = ug / n_v;
+        h = 2 * hh + (x >> 2);
+        j = n_t + (ug - hh * n_v);
+    } else {
+        const int v = x + kQueues * r;
+        h = v / n_v;
+        j = n_t + (v - h * n_v);
     }
+}
+
+// A workgroup first drains the queue of the XCD it runs on (read from the
+// hardware), then those of the other XCDs of its head group, then the rest:
+// XCDs that run faster take units from slower ones, and no slot idles while
+// work remains.  Returns the index of the next unit in queue `x`, or -1 when
+// every queue is empty.  `empty` collects the queues this workgroup has seen
+// exhausted.
+__device__ __forceinline__ int next_unit(uint32_t* sched, int H, int n_t, int n_v, int n_a, int xcc,
+                                         uint32_t& empty, int& x) {
+    const int D = H * (n_t + n_a);
+#pragma unroll 1
+    for (int s = 0; s < kQueues; ++s) {
+        x = ((xcc + (s & 4)) & 4) | ((xcc + s) & 3);
+        if ((empty >> x) & 1u) continue;
+        const int count = dense_begin(D, x + 1) - dense_begin(D, x) + video_count(H, n_v, x);
+        uint32_t i = 0;
+        if (threadIdx.x == 0) i = atomicAdd(sched + 32 * x, 1u);
+        i = __builtin_amdgcn_readfirstlane(i);
+        if ((int)i < count) return (int)i;
+        empty |= 1u << x;
+    }
+    return -1;
+}
+
+__global__ void clear_sched_kernel(uint32_t* sched) {
+    for (int i = threadIdx.x; i < 32 * kQueues; i += blockDim.x) sched[i] = 0u;
 }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -269,289 +299,322 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
     const uint32_t vslot[2] = {lds0 + 24576u, lds0 + 32768u};
     auto kslot = [&](int i) -> uint32_t { return lds0 + 8192u * (uint32_t)i; };
 
-    int h, j;
-    unit_of(blockIdx.x, a.H, a.n_t, a.n_v, a.n_a, h, j);
-    if (h >= a.H || j >= a.N) return;  // not reached: the map is a bijection onto the units
-    const int lane = threadIdx.x, g = lane >> 5, l32 = lane & 31;
-    const int64_t rs = (int64_t)a.H * kD;  // elements between consecutive tokens
-    const bool video = j >= a.n_t && j < a.n_t + a.n_v;
-    const int u = j - a.n_t;
-    const int n_tiles = video ? a.n_t + a.kk + a.n_a : a.N;
-    const int32_t* selrow = a.sel + ((int64_t)h * a.n_v + (video ? u : 0)) * a.kk;
-    const float c2 = a.scale_log2;
+    const int xcc = (int)(__builtin_amdgcn_s_getreg(kHwRegXccId) & (kQueues - 1));
+    uint32_t empty = 0;
+#pragma unroll 1
+    for (;;) {
+        int qx;
+        const int qi = next_unit(a.sched, a.H, a.n_t, a.n_v, a.n_a, xcc, empty, qx);
+        if (qi < 0) break;
+        // the lane index passes through an opaque move in every iteration, so the
+        // compiler keeps no lane-dependent address of the unit body live across
+        // units (hoisting them out of this loop would spill)
+        int lane;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(lane) : "v"((int)threadIdx.x));
+        const int g = lane >> 5, l32 = lane & 31;
+        int h, j;
+        queue_unit(a.H, a.n_t, a.n_v, a.n_a, qx, qi, h, j);
+        if (h >= a.H || j >= a.N) break;  // not reached: the queues partition the units
+        const int64_t rs = (int64_t)a.H * kD;  // elements between consecutive tokens
+        const bool video = j >= a.n_t && j < a.n_t + a.n_v;
+        const int u = j - a.n_t;
+        const int n_tiles = video ? a.n_t + a.kk + a.n_a : a.N;
+        const int32_t* selrow = a.sel + ((int64_t)h * a.n_v + (video ? u : 0)) * a.kk;
+        const float c2 = a.scale_log2;
 
-    // position `it` of this unit's ascending key-tile list -> tile index;
-    // positions past the end name the last tile
-    auto tile_at = [&](int it) -> int {
-        if (it >= n_tiles) it = n_tiles - 1;
-        if (!video || it < a.n_t) return it;
-        if (it < a.n_t + a.kk) {
-            // caller-supplied index sets are clamped into range, never followed out of bounds
-            const int w = load_uniform(selrow + (it - a.n_t));
-            return a.n_t + (w < 0 ? 0 : (w >= a.n_v ? a.n_v - 1 : w));
-        }
-        return a.n_v + it - a.kk;
-    };
-    // per-head bases of the packed operands (bytes): 16 KiB per tile and
-    // tensor, two 8 KiB half-tiles each
-    const char* kbase = (const char*)(a.kpack + (int64_t)h * a.N * (kT * kD));
-    const char* vbase = (const char*)(a.vpack + (int64_t)h * a.N * (kT * kD));
-    constexpr int64_t kTileBytes = 2 * kTileElems;
-    constexpr int64_t kHalfBytes = 2 * kHalfElems;
-    uint32_t voff[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) voff[i] = 16u * lane + 1024u * i;
-    auto fetch_k = [&](uint32_t slot, int tile, int half) {
-        fetch_half(slot, kbase + tile * kTileBytes + half * kHalfBytes, voff);
-    };
-    auto fetch_v = [&](uint32_t slot, int tile, int half) {
-        fetch_half(slot, vbase + tile * kTileBytes + half * kHalfBytes, voff);
-    };
-
-    // Q^T fragments (B operand of S^T = K Q^T): query l32 of block qb, dims 16s + 8g .. +7
-    bf16x8 qf[2][8];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const uint16_t* qp = a.q + ((int64_t)j * kT + 32 * qb + l32) * rs + (int64_t)h * kD + 8 * g;
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) qf[qb][s8] = *(const bf16x8*)(qp + 16 * s8);
-    }
-    wait_vmcnt(0);  // Q is resident before the ring starts counting loads
-    // padding query rows (past the tile's token rows) attend with zeros and
-    // are written as zeros
-    const int nq = tile_rows(a, j);
-    if (nq < kT) {
-        bf16x8 z8;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) z8[i] = (__bf16)0.0f;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-            if (32 * qb + l32 >= nq)
-#pragma unroll
-                for (int s8 = 0; s8 < 8; ++s8) qf[qb][s8] = z8;
-    }
-
-    const int t0 = tile_at(0), t1 = tile_at(1);
-
-    // Softmax reference.  Each column uses one fixed reference m_ref (in units
-    // of scale_log2 * score) for its whole key list: P = 2^(x - m_ref), and O
-    // and l accumulate without any rescaling.  m_ref starts at the column max
-    // of the first half-tile, so the largest P of that half-tile is 1.  If a
-    // later score exceeds it by so much that the denominator passes 2^100 (or
-    // overflows), the unit is recomputed with m_ref raised by log2 of the
-    // denominator (by 126 if it overflowed); the result is the same softmax,
-    // and for ordinary inputs the first pass is the only pass.
-    float m_ref[2];
-    f32x16 o[2][4];
-    float l_run[2];
-    f32x16 zero16;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) zero16[i] = 0.0f;
-    bf16x8 zero8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) zero8[i] = (__bf16)0.0f;
-    for (int pass = 0;; ++pass) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-            l_run[qb] = 0.0f;
-#pragma unroll
-            for (int db = 0; db < 4; ++db) o[qb][db] = zero16;
-        }
-        // Half-tile x of the list: K(x) and V(x) are half (x & 1) of tile
-        // (x >> 1), staged in K slot x mod 3 and V slot x mod 2.  Step x
-        // computes
-        //   S^T(x+1) = K(x+1) Q^T              (16 MFMAs)
-        //   P(x)     = numerators of S^T(x)     (vector ALU)
-        //   O       += V(x-1) P(x-1)            (16 MFMAs)
-        // so none of its matrix work waits for its own vector work.  Operands
-        // enter registers one step ahead (K(x+2) in the middle of step x,
-        // V(x) at its end).  Step x fetches V(x+1), one 1 KiB piece after
-        // each pair of S^T MFMAs, and then K(x+4), one piece after each pair
-        // of PV MFMAs, so the copies issue while the matrix unit is busy; a
-        // K half-tile has about two steps to arrive and a V half-tile two.
-        // In issue order, K(x+2) is complete once at most 24 fetches are
-        // outstanding at the middle of the step (V(x), K(x+3) of step x-1 and
-        // V(x+1)), and V(x) once at most 24 are at its end (K(x+3), V(x+1),
-        // K(x+4)).
-        bf16x8 kop[8], vop[8];
-        bf16x8 pprev[2][2];
-        f32x16 sc[2];
-        // prologue: K(0), K(1), K(2); S^T(0); then V(0), K(3) as the fetches
-        // of step -1; PV(-1) multiplies zeros
-        fetch_k(kslot(0), t0, 0);
-        fetch_k(kslot(1), t0, 1);
-        fetch_k(kslot(2), t1, 0);
-        wait_vmcnt(16);
-        read_ops(kop, kslot(0), lane);
-        sc[0] = zero16;
-        sc[1] = zero16;
-#pragma unroll
-        for (int s8 = 0; s8 < 8; ++s8) {
-            sc[0] = mfma32(kop[s8], qf[0][s8], sc[0]);
-            sc[1] = mfma32(kop[s8], qf[1][s8], sc[1]);
-        }
-        wait_vmcnt(8);
-        wait_lgkm();
-        read_ops(kop, kslot(1), lane);
-        fetch_v(vslot[0], t0, 0);
-        fetch_k(kslot(0), t1, 1);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vop[i] = zero8;
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) pprev[qb][0] = pprev[qb][1] = zero8;
-        {
-            const int nv0 = tile_rows(a, t0);  // S^T(0) is half 0 of the first tile
-            if (nv0 < 32) {
-                mask_keys(sc[0], nv0, g);
-                mask_keys(sc[1], nv0, g);
+        // position `it` of this unit's ascending key-tile list -> tile index;
+        // positions past the end name the last tile
+        auto tile_at = [&](int it) -> int {
+            if (it >= n_tiles) it = n_tiles - 1;
+            if (!video || it < a.n_t) return it;
+            if (it < a.n_t + a.kk) {
+                // caller-supplied index sets are clamped into range, never followed out of bounds
+                const int w = load_uniform(selrow + (it - a.n_t));
+                return a.n_t + (w < 0 ? 0 : (w >= a.n_v ? a.n_v - 1 : w));
             }
+            return a.n_v + it - a.kk;
+        };
+        // per-head bases of the packed operands (bytes): 16 KiB per tile and
+        // tensor, two 8 KiB half-tiles each
+        const char* kbase = (const char*)(a.kpack + (int64_t)h * a.N * (kT * kD));
+        const char* vbase = (const char*)(a.vpack + (int64_t)h * a.N * (kT * kD));
+        constexpr int64_t kTileBytes = 2 * kTileElems;
+        constexpr int64_t kHalfBytes = 2 * kHalfElems;
+        uint32_t voff[8];
+    #pragma unroll
+        for (int i = 0; i < 8; ++i) voff[i] = 16u * lane + 1024u * i;
+        auto fetch_k = [&](uint32_t slot, int tile, int half) {
+            fetch_half(slot, kbase + tile * kTileBytes + half * kHalfBytes, voff);
+        };
+        auto fetch_v = [&](uint32_t slot, int tile, int half) {
+            fetch_half(slot, vbase + tile * kTileBytes + half * kHalfBytes, voff);
+        };
+
+        // Q^T fragments (B operand of S^T = K Q^T): query l32 of block qb, dims 16s + 8g .. +7
+        bf16x8 qf[2][8];
+    #pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const uint16_t* qp = a.q + ((int64_t)j * kT + 32 * qb + l32) * rs + (int64_t)h * kD + 8 * g;
+    #pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) qf[qb][s8] = *(const bf16x8*)(qp + 16 * s8);
         }
-        if (pass == 0) {
-            m_ref[0] = column_max(sc[0], c2);
-            m_ref[1] = column_max(sc[1], c2);
+        wait_vmcnt(0);  // Q is resident before the ring starts counting loads
+        // padding query rows (past the tile's token rows) attend with zeros and
+        // are written as zeros
+        const int nq = tile_rows(a, j);
+        if (nq < kT) {
+            bf16x8 z8;
+    #pragma unroll
+            for (int i = 0; i < 8; ++i) z8[i] = (__bf16)0.0f;
+    #pragma unroll
+            for (int qb = 0; qb < 2; ++qb)
+                if (32 * qb + l32 >= nq)
+    #pragma unroll
+                    for (int s8 = 0; s8 < 8; ++s8) qf[qb][s8] = z8;
         }
 
-        // tiles of list positions t, t+1 (cur, nxt) carried across iterations;
-        // xm3 = x mod 3 for the current step x
-        int cur = t0, nxt = t1;
-        int xm3 = 0;
-        for (int t = 0; t < n_tiles; ++t) {
-            const int nn = tile_at(t + 2);
-            const int rows_cur = tile_rows(a, cur);  // token rows of the tile in use
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-                // step x = 2t + pp
-                const int k_wr = xm3 == 2 ? 0 : xm3 + 1;  // (x + 4) mod 3
-                const int k_rd = xm3 == 0 ? 2 : xm3 - 1;  // (x + 2) mod 3
-                wait_lgkm();  // kop = K(x+1), vop = V(x-1)
-                // V(x+1): (t, half 1) or (t+1, half 0); K(x+4): (t+2, half pp),
-                // issued one 1 KiB piece at a time between MFMAs below
-                const char* vsrc = vbase + (pp == 0 ? cur : nxt) * kTileBytes + (pp ^ 1) * kHalfBytes;
-                const char* ksrc = kbase + nn * kTileBytes + pp * kHalfBytes;
-                const uint32_t vdst = vslot[pp ^ 1], kdst = kslot(k_wr);
-                f32x16 n0 = zero16, n1 = zero16;
-                bf16x8 pc[2][2];
-                {
-                    // keys of half pp of the current tile that are tokens
-                    const int nvh = rows_cur - 32 * pp;
-                    if (nvh < 32) {
-                        mask_keys(sc[0], nvh, g);
-                        mask_keys(sc[1], nvh, g);
+        const int t0 = tile_at(0), t1 = tile_at(1);
+
+        // Softmax reference.  Each column uses one fixed reference m_ref (in units
+        // of scale_log2 * score) for its whole key list: P = 2^(x - m_ref), and O
+        // and l accumulate without any rescaling.  m_ref starts at the column max
+        // of the first half-tile, so the largest P of that half-tile is 1.  If a
+        // later score exceeds it by so much that the denominator passes 2^100 (or
+        // overflows), the unit is recomputed with m_ref raised by log2 of the
+        // denominator (by 126 if it overflowed); the result is the same softmax,
+        // and for ordinary inputs the first pass is the only pass.
+        float m_ref[2];
+        f32x16 o[2][4];
+        float l_run[2];
+        f32x16 zero16;
+    #pragma unroll
+        for (int i = 0; i < 16; ++i) zero16[i] = 0.0f;
+        bf16x8 zero8;
+    #pragma unroll
+        for (int i = 0; i < 8; ++i) zero8[i] = (__bf16)0.0f;
+        for (int pass = 0;; ++pass) {
+    #pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+                l_run[qb] = 0.0f;
+    #pragma unroll
+                for (int db = 0; db < 4; ++db) o[qb][db] = zero16;
+            }
+            // Half-tile x of the list: K(x) and V(x) are half (x & 1) of tile
+            // (x >> 1), staged in K slot x mod 3 and V slot x mod 2.  Step x
+            // computes
+            //   S^T(x+1) = K(x+1) Q^T              (16 MFMAs)
+            //   P(x)     = numerators of S^T(x)     (vector ALU)
+            //   O       += V(x-1) P(x-1)            (16 MFMAs)
+            // so none of its matrix work waits for its own vector work.  Operands
+            // enter registers one step ahead (K(x+2) in the middle of step x,
+            // V(x) at its end).  Step x fetches V(x+1), one 1 KiB piece after
+            // each pair of S^T MFMAs, and then K(x+4), one piece after each pair
+            // of PV MFMAs, so the copies issue while the matrix unit is busy; a
+            // K half-tile has about two steps to arrive and a V half-tile two.
+            // In issue order, K(x+2) is complete once at most 24 fetches are
+            // outstanding at the middle of the step (V(x), K(x+3) of step x-1 and
+            // V(x+1)), and V(x) once at most 24 are at its end (K(x+3), V(x+1),
+            // K(x+4)).
+            bf16x8 kop[8], vop[8];
+            bf16x8 pprev[2][2];
+            f32x16 sc[2];
+            // prologue: K(0), K(1), K(2); S^T(0); then V(0), K(3) as the fetches
+            // of step -1; PV(-1) multiplies zeros
+            fetch_k(kslot(0), t0, 0);
+            fetch_k(kslot(1), t0, 1);
+            fetch_k(kslot(2), t1, 0);
+            wait_vmcnt(16);
+            read_ops(kop, kslot(0), lane);
+            sc[0] = zero16;
+            sc[1] = zero16;
+    #pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) {
+                sc[0] = mfma32(kop[s8], qf[0][s8], sc[0]);
+                sc[1] = mfma32(kop[s8], qf[1][s8], sc[1]);
+            }
+            wait_vmcnt(8);
+            wait_lgkm();
+            read_ops(kop, kslot(1), lane);
+            fetch_v(vslot[0], t0, 0);
+            fetch_k(kslot(0), t1, 1);
+    #pragma unroll
+            for (int i = 0; i < 8; ++i) vop[i] = zero8;
+    #pragma unroll
+            for (int qb = 0; qb < 2; ++qb) pprev[qb][0] = pprev[qb][1] = zero8;
+            {
+                const int nv0 = tile_rows(a, t0);  // S^T(0) is half 0 of the first tile
+                if (nv0 < 32) {
+                    mask_keys(sc[0], nv0, g);
+                    mask_keys(sc[1], nv0, g);
+                }
+            }
+            if (pass == 0) {
+                m_ref[0] = column_max(sc[0], c2);
+                m_ref[1] = column_max(sc[1], c2);
+            }
+
+            // tiles of list positions t, t+1 (cur, nxt) carried across iterations;
+            // xm3 = x mod 3 for the current step x
+            int cur = t0, nxt = t1;
+            int xm3 = 0;
+            for (int t = 0; t < n_tiles; ++t) {
+                const int nn = tile_at(t + 2);
+                const int rows_cur = tile_rows(a, cur);  // token rows of the tile in use
+    #pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    // step x = 2t + pp
+                    const int k_wr = xm3 == 2 ? 0 : xm3 + 1;  // (x + 4) mod 3
+                    const int k_rd = xm3 == 0 ? 2 : xm3 - 1;  // (x + 2) mod 3
+                    wait_lgkm();  // kop = K(x+1), vop = V(x-1)
+                    // V(x+1): (t, half 1) or (t+1, half 0); K(x+4): (t+2, half pp),
+                    // issued one 1 KiB piece at a time between MFMAs below
+                    const char* vsrc = vbase + (pp == 0 ? cur : nxt) * kTileBytes + (pp ^ 1) * kHalfBytes;
+                    const char* ksrc = kbase + nn * kTileBytes + pp * kHalfBytes;
+                    const uint32_t vdst = vslot[pp ^ 1], kdst = kslot(k_wr);
+                    f32x16 n0 = zero16, n1 = zero16;
+                    bf16x8 pc[2][2];
+                    {
+                        // keys of half pp of the current tile that are tokens
+                        const int nvh = rows_cur - 32 * pp;
+                        if (nvh < 32) {
+                            mask_keys(sc[0], nvh, g);
+                            mask_keys(sc[1], nvh, g);
+                        }
                     }
-                }
-#pragma unroll
-                for (int s8 = 0; s8 < 8; ++s8) {
-                    n0 = mfma32(kop[s8], qf[0][s8], n0);
-                    n1 = mfma32(kop[s8], qf[1][s8], n1);
-                    fetch_piece(vdst + 1024u * s8, vsrc, voff[s8]);
-                    __builtin_amdgcn_sched_barrier(0x406);
-                }
-                numerators(sc[0], c2, m_ref[0], l_run[0], pc[0][0], pc[0][1]);
-                wait_vmcnt(24);  // K(x+2)
-                read_ops(kop, kslot(k_rd), lane);
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-#pragma unroll
-                    for (int m = 0; m < 2; ++m) {
-                        o[0][db] = mfma32(vop[2 * db + m], pprev[0][m], o[0][db]);
-                        o[1][db] = mfma32(vop[2 * db + m], pprev[1][m], o[1][db]);
-                        fetch_piece(kdst + 1024u * (2 * db + m), ksrc, voff[2 * db + m]);
+    #pragma unroll
+                    for (int s8 = 0; s8 < 8; ++s8) {
+                        n0 = mfma32(kop[s8], qf[0][s8], n0);
+                        n1 = mfma32(kop[s8], qf[1][s8], n1);
+                        fetch_piece(vdst + 1024u * s8, vsrc, voff[s8]);
                         __builtin_amdgcn_sched_barrier(0x406);
                     }
-                numerators(sc[1], c2, m_ref[1], l_run[1], pc[1][0], pc[1][1]);
-                wait_vmcnt(24);  // V(x)
-                read_ops(vop, vslot[pp], lane);
-                sc[0] = n0;
-                sc[1] = n1;
-#pragma unroll
-                for (int qb = 0; qb < 2; ++qb) {
-                    pprev[qb][0] = pc[qb][0];
-                    pprev[qb][1] = pc[qb][1];
+                    numerators(sc[0], c2, m_ref[0], l_run[0], pc[0][0], pc[0][1]);
+                    wait_vmcnt(24);  // K(x+2)
+                    read_ops(kop, kslot(k_rd), lane);
+    #pragma unroll
+                    for (int db = 0; db < 4; ++db)
+    #pragma unroll
+                        for (int m = 0; m < 2; ++m) {
+                            o[0][db] = mfma32(vop[2 * db + m], pprev[0][m], o[0][db]);
+                            o[1][db] = mfma32(vop[2 * db + m], pprev[1][m], o[1][db]);
+                            fetch_piece(kdst + 1024u * (2 * db + m), ksrc, voff[2 * db + m]);
+                            __builtin_amdgcn_sched_barrier(0x406);
+                        }
+                    numerators(sc[1], c2, m_ref[1], l_run[1], pc[1][0], pc[1][1]);
+                    wait_vmcnt(24);  // V(x)
+                    read_ops(vop, vslot[pp], lane);
+                    sc[0] = n0;
+                    sc[1] = n1;
+    #pragma unroll
+                    for (int qb = 0; qb < 2; ++qb) {
+                        pprev[qb][0] = pc[qb][0];
+                        pprev[qb][1] = pc[qb][1];
+                    }
+                    xm3 = k_wr;  // (x + 1) mod 3
                 }
-                xm3 = k_wr;  // (x + 1) mod 3
+                cur = nxt;
+                nxt = nn;
             }
-            cur = nxt;
-            nxt = nn;
+            // the last PV
+            wait_lgkm();
+    #pragma unroll
+            for (int db = 0; db < 4; ++db)
+    #pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    o[0][db] = mfma32(vop[2 * db + m], pprev[0][m], o[0][db]);
+                    o[1][db] = mfma32(vop[2 * db + m], pprev[1][m], o[1][db]);
+                }
+            wait_vmcnt(0);
+            l_run[0] = xhalf_sum(l_run[0]);
+            l_run[1] = xhalf_sum(l_run[1]);
+            const bool big0 = !(l_run[0] <= 0x1p100f), big1 = !(l_run[1] <= 0x1p100f);
+            if (!__ballot(big0 || big1) || pass >= 3) break;
+            if (big0) m_ref[0] += l_run[0] <= 0x1p126f ? __log2f(l_run[0]) : 126.0f;
+            if (big1) m_ref[1] += l_run[1] <= 0x1p126f ? __log2f(l_run[1]) : 126.0f;
         }
-        // the last PV
-        wait_lgkm();
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                o[0][db] = mfma32(vop[2 * db + m], pprev[0][m], o[0][db]);
-                o[1][db] = mfma32(vop[2 * db + m], pprev[1][m], o[1][db]);
-            }
-        wait_vmcnt(0);
-        l_run[0] = xhalf_sum(l_run[0]);
-        l_run[1] = xhalf_sum(l_run[1]);
-        const bool big0 = !(l_run[0] <= 0x1p100f), big1 = !(l_run[1] <= 0x1p100f);
-        if (!__ballot(big0 || big1) || pass >= 3) break;
-        if (big0) m_ref[0] += l_run[0] <= 0x1p126f ? __log2f(l_run[0]) : 126.0f;
-        if (big1) m_ref[1] += l_run[1] <= 0x1p126f ? __log2f(l_run[1]) : 126.0f;
-    }
 
-    // ---- epilogue: normalise, stage through LDS, add sigmoid(G) * coarse ----
-    // Lane l writes dims 8(l%16) .. +7 of rows l/16 + 4i, i < 16.  The gate
-    // rows (never read before, so they come from HBM) and the lane's eight
-    // coarse values are all requested here, before the staging, so their
-    // latency is paid once per unit rather than once per group of rows.
-    const bool gated = video && a.gate;
-    const int c16 = lane & 15;
-    uint4 gw[16];
-    float4 cv0, cv1;
-    if (gated) {
-        const uint16_t* gp = a.gate + ((int64_t)j * kT + (lane >> 4)) * rs + (int64_t)h * kD + 8 * c16;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) gw[i] = *(const uint4*)(gp + 4 * i * rs);
-        const float* cp = a.coarse + ((int64_t)h * a.n_v + u) * kD + 8 * c16;
-        cv0 = *(const float4*)cp;
-        cv1 = *(const float4*)(cp + 4);
-    }
-    float* ost = (float*)lds;  // [64 queries][128 dims], 16-byte chunks swizzled by row
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-        const float inv = __builtin_amdgcn_rcpf(l_run[qb]);
-        const int q = 32 * qb + l32;
-        float* orow = ost + q * kD;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const int chunk = 8 * db + 2 * a4 + g;  // dims 4*chunk .. 4*chunk+3
-                *(float4*)(orow + 4 * (chunk ^ (q & 15))) =
-                    make_float4(o[qb][db][4 * a4 + 0] * inv, o[qb][db][4 * a4 + 1] * inv,
-                                o[qb][db][4 * a4 + 2] * inv, o[qb][db][4 * a4 + 3] * inv);
-            }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int row = (lane >> 4) + 4 * i, c = c16;
-        const float4 x0 = *(const float4*)(ost + row * kD + 4 * ((2 * c) ^ (row & 15)));
-        const float4 x1 = *(const float4*)(ost + row * kD + 4 * ((2 * c + 1) ^ (row & 15)));
-        f32x8 y = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        const int64_t grow = (int64_t)j * kT + row;
-        if (row >= nq) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = 0.0f;
-        } else if (gated) {
-            const uint32_t gwv[4] = {gw[i].x, gw[i].y, gw[i].z, gw[i].w};
-            const float cv[8] = {cv0.x, cv0.y, cv0.z, cv0.w, cv1.x, cv1.y, cv1.z, cv1.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                y[2 * e] += sigmoidf(__uint_as_float(gwv[e] << 16)) * cv[2 * e];
-                y[2 * e + 1] += sigmoidf(__uint_as_float(gwv[e] & 0xFFFF0000u)) * cv[2 * e + 1];
-            }
+        // ---- epilogue: normalise, stage through LDS, add sigmoid(G) * coarse ----
+        // Lane l writes dims 8(l%16) .. +7 of rows l/16 + 4i, i < 16.  The gate
+        // rows (never read before, so they come from HBM) and the lane's eight
+        // coarse values are all requested here, before the staging, so their
+        // latency is paid once per unit rather than once per group of rows.
+        const bool gated = video && a.gate;
+        const int c16 = lane & 15;
+        uint4 gw[16];
+        float4 cv0, cv1;
+        if (gated) {
+            const uint16_t* gp = a.gate + ((int64_t)j * kT + (lane >> 4)) * rs + (int64_t)h * kD + 8 * c16;
+    #pragma unroll
+            for (int i = 0; i < 16; ++i) gw[i] = *(const uint4*)(gp + 4 * i * rs);
+            const float* cp = a.coarse + ((int64_t)h * a.n_v + u) * kD + 8 * c16;
+            cv0 = *(const float4*)cp;
+            cv1 = *(const float4*)(cp + 4);
         }
-        *(bf16x8*)(a.out + grow * rs + (int64_t)h * kD + 8 * c) = __builtin_convertvector(y, bf16x8);
+        float* ost = (float*)lds;  // [64 queries][128 dims], 16-byte chunks swizzled by row
+    #pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+            const float inv = __builtin_amdgcn_rcpf(l_run[qb]);
+            const int q = 32 * qb + l32;
+            float* orow = ost + q * kD;
+    #pragma unroll
+            for (int db = 0; db < 4; ++db)
+    #pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const int chunk = 8 * db + 2 * a4 + g;  // dims 4*chunk .. 4*chunk+3
+                    *(float4*)(orow + 4 * (chunk ^ (q & 15))) =
+                        make_float4(o[qb][db][4 * a4 + 0] * inv, o[qb][db][4 * a4 + 1] * inv,
+                                    o[qb][db][4 * a4 + 2] * inv, o[qb][db][4 * a4 + 3] * inv);
+                }
+        }
+        __syncthreads();
+    #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int row = (lane >> 4) + 4 * i, c = c16;
+            const float4 x0 = *(const float4*)(ost + row * kD + 4 * ((2 * c) ^ (row & 15)));
+            const float4 x1 = *(const float4*)(ost + row * kD + 4 * ((2 * c + 1) ^ (row & 15)));
+            f32x8 y = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const int64_t grow = (int64_t)j * kT + row;
+            if (row >= nq) {
+    #pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+            } else if (gated) {
+                const uint32_t gwv[4] = {gw[i].x, gw[i].y, gw[i].z, gw[i].w};
+                const float cv[8] = {cv0.x, cv0.y, cv0.z, cv0.w, cv1.x, cv1.y, cv1.z, cv1.w};
+    #pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    y[2 * e] += sigmoidf(__uint_as_float(gwv[e] << 16)) * cv[2 * e];
+                    y[2 * e + 1] += sigmoidf(__uint_as_float(gwv[e] & 0xFFFF0000u)) * cv[2 * e + 1];
+                }
+            }
+            *(bf16x8*)(a.out + grow * rs + (int64_t)h * kD + 8 * c) = __builtin_convertvector(y, bf16x8);
+        }
+        // the next unit's copies overwrite the staging area
+        wait_lgkm();
+        __syncthreads();
     }
 }
 
 }  // namespace
 
+// Wavefront slots of the device: 4 per CU (40 KiB of LDS each), cached per device.
+int fine_slots() {
+    static std::atomic<int> slots[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 1024;
+    int n = slots[dev].load();
+    if (n == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        n = 4 * cus;
+        slots[dev].store(n);
+    }
+    return n;
+}
+
 hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate, const int32_t* sel,
-                                 uint16_t* out, const Shape& s, const uint8_t* ws, const Layout& L,
+                                 uint16_t* out, const Shape& s, uint8_t* ws, const Layout& L,
                                  hipStream_t stream) {
     FineArgs a;
     a.q = q;
@@ -561,6 +624,7 @@ hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate, const 
     a.sel = sel;
     a.coarse = (const float*)(ws + L.coarse);
     a.out = out;
+    a.sched = (uint32_t*)(ws + L.sched);
     a.H = s.H;
     a.n_t = s.n_t;
     a.n_v = s.n_v;
@@ -572,7 +636,13 @@ hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate, const 
     a.last_valid[2] = s.n_a ? (int)(s.V_a - 64 * (int64_t)(s.n_a - 1)) : kT;
     a.scale_log2 = (float)(1.4426950408889634 / 11.313708498984761);
     const int64_t units = (int64_t)s.H * s.N;
-    hipLaunchKernelGGL(fine_attn_kernel, dim3((unsigned)units), dim3(kThreads), 0, stream, a);
+    // counters start at zero (a kernel, not a memset node, so that the call
+    // can be recorded into a HIP graph)
+    hipLaunchKernelGGL(clear_sched_kernel, dim3(1), dim3(64), 0, stream, a.sched);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t grid = units < fine_slots() ? units : fine_slots();
+    hipLaunchKernelGGL(fine_attn_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -222,7 +222,7 @@ vsa_status vsa_fine_attention(const void* q, const void* gate, int32_t num_heads
     if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
     if ((st = check_device()) != VSA_OK) return st;
     return from_hip(vsa::launch_fine_attention((const uint16_t*)q, (const uint16_t*)gate, selected_tiles, (uint16_t*)out,
-                                               s, (const uint8_t*)workspace, L, (hipStream_t)stream));
+                                               s, (uint8_t*)workspace, L, (hipStream_t)stream));
 }
 
 vsa_status vsa_forward(const void* q, const void* k, const void* v, const void* gate,

@@ -50,6 +50,7 @@ struct Layout {
     size_t coarse;  // float  [H][n_v][128]
     size_t kpack;   // bf16   [H][N][2][8][64][8]      K tiles in MFMA A-operand order
     size_t vpack;   // bf16   [H][N][2][4][2][64][8]   V^T tiles in MFMA A-operand order
+    size_t sched;   // uint32 [8][32]  fine-attention work-queue counters (one 128-byte line each)
     size_t qsub;    // float  [H][n_c][8][64][4]  SubBlock router: Q sub-block means (0 bytes
     size_t ksub;    // float  [H][n_c][8][64][4]  without the router), n_c = ceil(n_v / 4)
     size_t total;
@@ -60,6 +61,10 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // Largest n_v the SubBlock router takes: 4 rows of n_v float64 scores fill
 // the 160 KiB of LDS, and the wavefront top-k holds 80 keys per lane.
 constexpr int kSubblockMaxTiles = 5120;
+
+// Fine-attention work queues: one counter per XCD, each on its own 128-byte line.
+constexpr int kQueues = 8;
+constexpr size_t kSchedBytes = kQueues * 128;
 
 inline Layout make_layout(const Shape& s, bool subblock = false) {
     Layout L;
@@ -72,6 +77,7 @@ inline Layout make_layout(const Shape& s, bool subblock = false) {
     L.kpack = off;  off = align_up(off + (size_t)s.H * (size_t)s.N * kT * kD * 2);
     L.vpack = off;  off = align_up(off + (size_t)s.H * (size_t)s.N * kT * kD * 2);
     const size_t sub = subblock ? (size_t)s.H * (size_t)((s.n_v + 3) / 4) * 2048 * sizeof(float) : 0;
+    L.sched = off;  off = align_up(off + kSchedBytes);
     L.qsub = off;   off = align_up(off + sub);
     L.ksub = off;   off = align_up(off + sub);
     L.total = off;
@@ -107,7 +113,7 @@ hipError_t launch_select_coarse(const Shape& s, int32_t* sel, uint8_t* ws, const
                                 hipStream_t stream);
 hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate,
                                  const int32_t* sel, uint16_t* out, const Shape& s,
-                                 const uint8_t* ws, const Layout& L, hipStream_t stream);
+                                 uint8_t* ws, const Layout& L, hipStream_t stream);
 
 // SubBlock router: sub-block means of Q and K, scores and top-k (s.k tiles).
 hipError_t launch_subblock_route(const uint16_t* q, const uint16_t* k, const Shape& s,
