@@ -52,6 +52,7 @@ constexpr int kThreads = 64;
 constexpr int kHwRegXccId = (31 << 11) | 20;
 constexpr int kHalfElems = 32 * kD;  // bf16 elements per packed half-tile (8 KiB)
 constexpr int kTileElems = 2 * kHalfElems;
+constexpr int kPartFloats = kT * kD + 2 * kT;  // one dense part's record (33,280 bytes)
 
 struct FineArgs {
     const uint16_t* q;
@@ -62,6 +63,8 @@ struct FineArgs {
     const float* coarse;
     uint16_t* out;
     uint32_t* sched;    // kQueues work-queue counters, 32 words apart, zero at launch
+    float* partial;     // dense parts: [dense unit][part][64 x 128 O, 64 l, 64 reference]
+    int parts;          // key-list parts per dense unit (1: no split)
     int H, n_t, n_v, n_a, N, kk;
     int last_valid[3];  // token rows in the last text / video / audio tile (64 when full)
     float scale_log2;   // log2(e) / sqrt(128)
@@ -94,20 +97,23 @@ __device__ __forceinline__ int video_count(int H, int n_v, int x) {
     return v > x ? (v - x + kQueues - 1) / kQueues : 0;
 }
 
-// Unit i of queue x -> (h, j).
-__device__ __forceinline__ void queue_unit(int H, int n_t, int n_v, int n_a, int x, int i, int& h,
-                                           int& j) {
+// Unit i of queue x -> (h, j) and, for a dense unit, its key-list part p.
+__device__ __forceinline__ void queue_unit(int H, int n_t, int n_v, int n_a, int P, int x, int i,
+                                           int& h, int& j, int& p) {
     const int n_h = n_t + n_a;
-    const int D = H * n_h;
+    const int D = H * P * n_h;
     const int d0 = dense_begin(D, x);
     const int nvx = video_count(H, n_v, x);
     const bool dense = i >= nvx;
     const int r = dense ? i - nvx : i;
+    p = 0;
     if (dense) {
         const int item = d0 + r;
-        h = item / n_h;
-        const int p = item - h * n_h;
-        j = p < n_t ? p : n_v + p;
+        const int hp = item / n_h;  // head-major, then part, then query tile
+        const int t = item - hp * n_h;
+        h = hp / P;
+        p = hp - h * P;
+        j = t < n_t ? t : n_v + t;
     } else if ((H & 1) == 0) {
         const int ug = (x & 3) + 4 * r;
         const int hh = ug / n_v;
@@ -126,9 +132,9 @@ __device__ __forceinline__ void queue_unit(int H, int n_t, int n_v, int n_a, int
 // work remains.  Returns the index of the next unit in queue `x`, or -1 when
 // every queue is empty.  `empty` collects the queues this workgroup has seen
 // exhausted.
-__device__ __forceinline__ int next_unit(uint32_t* sched, int H, int n_t, int n_v, int n_a, int xcc,
-                                         uint32_t& empty, int& x) {
-    const int D = H * (n_t + n_a);
+__device__ __forceinline__ int next_unit(uint32_t* sched, int H, int n_t, int n_v, int n_a, int P,
+                                         int xcc, uint32_t& empty, int& x) {
+    const int D = H * P * (n_t + n_a);
 #pragma unroll 1
     for (int s = 0; s < kQueues; ++s) {
         x = ((xcc + (s & 4)) & 4) | ((xcc + s) & 3);
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
 #pragma unroll 1
     for (;;) {
         int qx;
-        const int qi = next_unit(a.sched, a.H, a.n_t, a.n_v, a.n_a, xcc, empty, qx);
+        const int qi = next_unit(a.sched, a.H, a.n_t, a.n_v, a.n_a, a.parts, xcc, empty, qx);
         if (qi < 0) break;
         // the lane index passes through an opaque move in every iteration, so the
         // compiler keeps no lane-dependent address of the unit body live across
@@ -312,13 +318,19 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         int lane;
         asm volatile("v_mov_b32 %0, %1" : "=v"(lane) : "v"((int)threadIdx.x));
         const int g = lane >> 5, l32 = lane & 31;
-        int h, j;
-        queue_unit(a.H, a.n_t, a.n_v, a.n_a, qx, qi, h, j);
+        int h, j, part;
+        queue_unit(a.H, a.n_t, a.n_v, a.n_a, a.parts, qx, qi, h, j, part);
         if (h >= a.H || j >= a.N) break;  // not reached: the queues partition the units
         const int64_t rs = (int64_t)a.H * kD;  // elements between consecutive tokens
         const bool video = j >= a.n_t && j < a.n_t + a.n_v;
         const int u = j - a.n_t;
-        const int n_tiles = video ? a.n_t + a.kk + a.n_a : a.N;
+        // a dense unit's list (every tile) is walked as `parts` contiguous
+        // ranges by separate units whose unnormalised results are combined
+        // afterwards; part p covers tiles it0 .. it0 + n_tiles - 1
+        const bool split = !video && a.parts > 1;
+        const int it0 = video ? 0 : (int)((int64_t)part * a.N / a.parts);
+        const int n_tiles =
+            video ? a.n_t + a.kk + a.n_a : (int)((int64_t)(part + 1) * a.N / a.parts) - it0;
         const int32_t* selrow = a.sel + ((int64_t)h * a.n_v + (video ? u : 0)) * a.kk;
         const float c2 = a.scale_log2;
 
@@ -326,7 +338,8 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         // positions past the end name the last tile
         auto tile_at = [&](int it) -> int {
             if (it >= n_tiles) it = n_tiles - 1;
-            if (!video || it < a.n_t) return it;
+            if (!video) return it0 + it;
+            if (it < a.n_t) return it;
             if (it < a.n_t + a.kk) {
                 // caller-supplied index sets are clamped into range, never followed out of bounds
                 const int w = load_uniform(selrow + (it - a.n_t));
@@ -341,7 +354,7 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         constexpr int64_t kTileBytes = 2 * kTileElems;
         constexpr int64_t kHalfBytes = 2 * kHalfElems;
         uint32_t voff[8];
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < 8; ++i) voff[i] = 16u * lane + 1024u * i;
         auto fetch_k = [&](uint32_t slot, int tile, int half) {
             fetch_half(slot, kbase + tile * kTileBytes + half * kHalfBytes, voff);
@@ -352,10 +365,10 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
 
         // Q^T fragments (B operand of S^T = K Q^T): query l32 of block qb, dims 16s + 8g .. +7
         bf16x8 qf[2][8];
-    #pragma unroll
+#pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const uint16_t* qp = a.q + ((int64_t)j * kT + 32 * qb + l32) * rs + (int64_t)h * kD + 8 * g;
-    #pragma unroll
+#pragma unroll
             for (int s8 = 0; s8 < 8; ++s8) qf[qb][s8] = *(const bf16x8*)(qp + 16 * s8);
         }
         wait_vmcnt(0);  // Q is resident before the ring starts counting loads
@@ -364,12 +377,12 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         const int nq = tile_rows(a, j);
         if (nq < kT) {
             bf16x8 z8;
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 8; ++i) z8[i] = (__bf16)0.0f;
-    #pragma unroll
+#pragma unroll
             for (int qb = 0; qb < 2; ++qb)
                 if (32 * qb + l32 >= nq)
-    #pragma unroll
+#pragma unroll
                     for (int s8 = 0; s8 < 8; ++s8) qf[qb][s8] = z8;
         }
 
@@ -387,16 +400,16 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         f32x16 o[2][4];
         float l_run[2];
         f32x16 zero16;
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) zero16[i] = 0.0f;
         bf16x8 zero8;
-    #pragma unroll
+#pragma unroll
         for (int i = 0; i < 8; ++i) zero8[i] = (__bf16)0.0f;
         for (int pass = 0;; ++pass) {
-    #pragma unroll
+#pragma unroll
             for (int qb = 0; qb < 2; ++qb) {
                 l_run[qb] = 0.0f;
-    #pragma unroll
+#pragma unroll
                 for (int db = 0; db < 4; ++db) o[qb][db] = zero16;
             }
             // Half-tile x of the list: K(x) and V(x) are half (x & 1) of tile
@@ -427,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
             read_ops(kop, kslot(0), lane);
             sc[0] = zero16;
             sc[1] = zero16;
-    #pragma unroll
+#pragma unroll
             for (int s8 = 0; s8 < 8; ++s8) {
                 sc[0] = mfma32(kop[s8], qf[0][s8], sc[0]);
                 sc[1] = mfma32(kop[s8], qf[1][s8], sc[1]);
@@ -437,9 +450,9 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
             read_ops(kop, kslot(1), lane);
             fetch_v(vslot[0], t0, 0);
             fetch_k(kslot(0), t1, 1);
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 8; ++i) vop[i] = zero8;
-    #pragma unroll
+#pragma unroll
             for (int qb = 0; qb < 2; ++qb) pprev[qb][0] = pprev[qb][1] = zero8;
             {
                 const int nv0 = tile_rows(a, t0);  // S^T(0) is half 0 of the first tile
@@ -460,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
             for (int t = 0; t < n_tiles; ++t) {
                 const int nn = tile_at(t + 2);
                 const int rows_cur = tile_rows(a, cur);  // token rows of the tile in use
-    #pragma unroll
+#pragma unroll
                 for (int pp = 0; pp < 2; ++pp) {
                     // step x = 2t + pp
                     const int k_wr = xm3 == 2 ? 0 : xm3 + 1;  // (x + 4) mod 3
@@ -481,7 +494,7 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
                             mask_keys(sc[1], nvh, g);
                         }
                     }
-    #pragma unroll
+#pragma unroll
                     for (int s8 = 0; s8 < 8; ++s8) {
                         n0 = mfma32(kop[s8], qf[0][s8], n0);
                         n1 = mfma32(kop[s8], qf[1][s8], n1);
@@ -491,9 +504,9 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
                     numerators(sc[0], c2, m_ref[0], l_run[0], pc[0][0], pc[0][1]);
                     wait_vmcnt(24);  // K(x+2)
                     read_ops(kop, kslot(k_rd), lane);
-    #pragma unroll
+#pragma unroll
                     for (int db = 0; db < 4; ++db)
-    #pragma unroll
+#pragma unroll
                         for (int m = 0; m < 2; ++m) {
                             o[0][db] = mfma32(vop[2 * db + m], pprev[0][m], o[0][db]);
                             o[1][db] = mfma32(vop[2 * db + m], pprev[1][m], o[1][db]);
@@ -505,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
                     read_ops(vop, vslot[pp], lane);
                     sc[0] = n0;
                     sc[1] = n1;
-    #pragma unroll
+#pragma unroll
                     for (int qb = 0; qb < 2; ++qb) {
                         pprev[qb][0] = pc[qb][0];
                         pprev[qb][1] = pc[qb][1];
@@ -517,9 +530,9 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
             }
             // the last PV
             wait_lgkm();
-    #pragma unroll
+#pragma unroll
             for (int db = 0; db < 4; ++db)
-    #pragma unroll
+#pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     o[0][db] = mfma32(vop[2 * db + m], pprev[0][m], o[0][db]);
                     o[1][db] = mfma32(vop[2 * db + m], pprev[1][m], o[1][db]);
@@ -544,21 +557,21 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         float4 cv0, cv1;
         if (gated) {
             const uint16_t* gp = a.gate + ((int64_t)j * kT + (lane >> 4)) * rs + (int64_t)h * kD + 8 * c16;
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < 16; ++i) gw[i] = *(const uint4*)(gp + 4 * i * rs);
             const float* cp = a.coarse + ((int64_t)h * a.n_v + u) * kD + 8 * c16;
             cv0 = *(const float4*)cp;
             cv1 = *(const float4*)(cp + 4);
         }
         float* ost = (float*)lds;  // [64 queries][128 dims], 16-byte chunks swizzled by row
-    #pragma unroll
+#pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-            const float inv = __builtin_amdgcn_rcpf(l_run[qb]);
+            const float inv = split ? 1.0f : __builtin_amdgcn_rcpf(l_run[qb]);
             const int q = 32 * qb + l32;
             float* orow = ost + q * kD;
-    #pragma unroll
+#pragma unroll
             for (int db = 0; db < 4; ++db)
-    #pragma unroll
+#pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
                     const int chunk = 8 * db + 2 * a4 + g;  // dims 4*chunk .. 4*chunk+3
                     *(float4*)(orow + 4 * (chunk ^ (q & 15))) =
@@ -567,7 +580,30 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
                 }
         }
         __syncthreads();
-    #pragma unroll
+        if (split) {
+            // unnormalised O, the denominators and the references of this part
+            float* pp = a.partial + (((int64_t)h * (a.n_t + a.n_a) + (j < a.n_t ? j : j - a.n_v)) *
+                                         a.parts + part) * kPartFloats;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = (lane >> 4) + 4 * i, c = c16;
+                *(float4*)(pp + row * kD + 8 * c) =
+                    *(const float4*)(ost + row * kD + 4 * ((2 * c) ^ (row & 15)));
+                *(float4*)(pp + row * kD + 8 * c + 4) =
+                    *(const float4*)(ost + row * kD + 4 * ((2 * c + 1) ^ (row & 15)));
+            }
+            if (g == 0) {
+#pragma unroll
+                for (int qb = 0; qb < 2; ++qb) {
+                    pp[kT * kD + 32 * qb + l32] = l_run[qb];
+                    pp[kT * kD + kT + 32 * qb + l32] = m_ref[qb];
+                }
+            }
+            wait_lgkm();
+            __syncthreads();
+            continue;
+        }
+#pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int row = (lane >> 4) + 4 * i, c = c16;
             const float4 x0 = *(const float4*)(ost + row * kD + 4 * ((2 * c) ^ (row & 15)));
@@ -575,12 +611,12 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
             f32x8 y = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
             const int64_t grow = (int64_t)j * kT + row;
             if (row >= nq) {
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 8; ++e) y[e] = 0.0f;
             } else if (gated) {
                 const uint32_t gwv[4] = {gw[i].x, gw[i].y, gw[i].z, gw[i].w};
                 const float cv[8] = {cv0.x, cv0.y, cv0.z, cv0.w, cv1.x, cv1.y, cv1.z, cv1.w};
-    #pragma unroll
+#pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     y[2 * e] += sigmoidf(__uint_as_float(gwv[e] << 16)) * cv[2 * e];
                     y[2 * e + 1] += sigmoidf(__uint_as_float(gwv[e] & 0xFFFF0000u)) * cv[2 * e + 1];
@@ -594,7 +630,59 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
     }
 }
 
+// Combination of a split dense unit's parts: with references m_p and
+// denominators l_p (per query row), O = sum_p O_p 2^(m_p - M) and
+// l = sum_p l_p 2^(m_p - M), M = max_p m_p; out = O / l, in part order.
+// One workgroup per dense unit; thread t covers rows t/16 + 16i, dims
+// 8(t%16) .. +7.
+__global__ __launch_bounds__(256) void combine_parts_kernel(FineArgs a) {
+    const int n_h = a.n_t + a.n_a;
+    const int du = blockIdx.x;  // h * n_h + dense tile
+    const int h = du / n_h, t = du - h * n_h;
+    const int j = t < a.n_t ? t : a.n_v + t;
+    const int nq = tile_rows(a, j);
+    const int64_t rs = (int64_t)a.H * kD;
+    const float* base = a.partial + (int64_t)du * a.parts * kPartFloats;
+    const int c = threadIdx.x & 15;
+#pragma unroll 1
+    for (int i = 0; i < 4; ++i) {
+        const int row = (threadIdx.x >> 4) + 16 * i;
+        f32x8 y;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = 0.0f;
+        if (row < nq) {
+            float mx = -__builtin_inff();
+            for (int p = 0; p < a.parts; ++p) mx = fmaxf(mx, base[p * kPartFloats + kT * kD + kT + row]);
+            float l = 0.0f;
+            for (int p = 0; p < a.parts; ++p) {
+                const float* pp = base + p * kPartFloats;
+                const float w = __builtin_amdgcn_exp2f(pp[kT * kD + kT + row] - mx);
+                l += w * pp[kT * kD + row];
+                const float4 x0 = *(const float4*)(pp + row * kD + 8 * c);
+                const float4 x1 = *(const float4*)(pp + row * kD + 8 * c + 4);
+                y[0] += w * x0.x; y[1] += w * x0.y; y[2] += w * x0.z; y[3] += w * x0.w;
+                y[4] += w * x1.x; y[5] += w * x1.y; y[6] += w * x1.z; y[7] += w * x1.w;
+            }
+            const float inv = __builtin_amdgcn_rcpf(l);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] *= inv;
+        }
+        *(bf16x8*)(a.out + ((int64_t)j * kT + row) * rs + (int64_t)h * kD + 8 * c) =
+            __builtin_convertvector(y, bf16x8);
+    }
+}
+
 }  // namespace
+
+// Key-list parts of a dense unit: about the length of a video unit's list
+// (so that no unit is much longer than the rest), at most kMaxParts; 1
+// without video tiles.
+int dense_parts(const Shape& s) {
+    if (s.n_v == 0 || s.n_t + s.n_a == 0) return 1;
+    const int lv = s.n_t + s.k + s.n_a;
+    int p = (int)((double)s.N / (double)lv + 0.5);
+    return p < 1 ? 1 : (p > kMaxParts ? kMaxParts : p);
+}
 
 // Wavefront slots of the device: 4 per CU (40 KiB of LDS each), cached per device.
 int fine_slots() {
@@ -625,6 +713,8 @@ hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate, const 
     a.coarse = (const float*)(ws + L.coarse);
     a.out = out;
     a.sched = (uint32_t*)(ws + L.sched);
+    a.partial = (float*)(ws + L.partial);
+    a.parts = dense_parts(s);
     a.H = s.H;
     a.n_t = s.n_t;
     a.n_v = s.n_v;
@@ -643,6 +733,10 @@ hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate, const 
     if (e != hipSuccess) return e;
     const int64_t grid = units < fine_slots() ? units : fine_slots();
     hipLaunchKernelGGL(fine_attn_kernel, dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess || a.parts == 1) return e;
+    hipLaunchKernelGGL(combine_parts_kernel, dim3((unsigned)(s.H * (s.n_t + s.n_a))), dim3(256), 0,
+                       stream, a);
     return hipGetLastError();
 }
 

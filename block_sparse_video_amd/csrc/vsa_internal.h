@@ -50,6 +50,7 @@ struct Layout {
     size_t coarse;  // float  [H][n_v][128]
     size_t kpack;   // bf16   [H][N][2][8][64][8]      K tiles in MFMA A-operand order
     size_t vpack;   // bf16   [H][N][2][4][2][64][8]   V^T tiles in MFMA A-operand order
+    size_t partial; // float  [H][n_t+n_a][parts][64*128 + 128]  split dense units' partial results
     size_t sched;   // uint32 [8][32]  fine-attention work-queue counters (one 128-byte line each)
     size_t qsub;    // float  [H][n_c][8][64][4]  SubBlock router: Q sub-block means (0 bytes
     size_t ksub;    // float  [H][n_c][8][64][4]  without the router), n_c = ceil(n_v / 4)
@@ -65,6 +66,11 @@ constexpr int kSubblockMaxTiles = 5120;
 // Fine-attention work queues: one counter per XCD, each on its own 128-byte line.
 constexpr int kQueues = 8;
 constexpr size_t kSchedBytes = kQueues * 128;
+// A dense (text/audio query) unit's key list is split into at most this many
+// parts; one part's record is 64 x 128 unnormalised outputs, 64 denominators
+// and 64 softmax references, float32.
+constexpr int kMaxParts = 4;
+constexpr size_t kPartBytes = (64 * 128 + 128) * sizeof(float);
 
 inline Layout make_layout(const Shape& s, bool subblock = false) {
     Layout L;
@@ -77,6 +83,8 @@ inline Layout make_layout(const Shape& s, bool subblock = false) {
     L.kpack = off;  off = align_up(off + (size_t)s.H * (size_t)s.N * kT * kD * 2);
     L.vpack = off;  off = align_up(off + (size_t)s.H * (size_t)s.N * kT * kD * 2);
     const size_t sub = subblock ? (size_t)s.H * (size_t)((s.n_v + 3) / 4) * 2048 * sizeof(float) : 0;
+    const size_t dense_units = (size_t)s.H * (size_t)(s.n_t + s.n_a);
+    L.partial = off; off = align_up(off + (s.n_v > 0 ? dense_units * kMaxParts * kPartBytes : 0));
     L.sched = off;  off = align_up(off + kSchedBytes);
     L.qsub = off;   off = align_up(off + sub);
     L.ksub = off;   off = align_up(off + sub);
