@@ -259,6 +259,33 @@ def test_late_large_scores_recompute():
     print(e)
 
 
+def test_split_dense_units_combine_parts():
+    """A text/audio query tile's key list is walked as several parts (here
+    3: N = 24 tiles, video lists of 8) whose outputs are merged with weights
+    2^(m_p - max m).  Scores grow by ~0.5 (log2 units) per key tile, so the
+    three parts start from references about 4 apart and all contribute; a
+    merge that ignored the references would be far off.  Video query tiles
+    select the last k video tiles (pooled scores grow with the tile index)."""
+    announce("split dense units: h=1 tiles=(2,20,2)")
+    h, s_t, n_v, s_a = 1, 128, 20, 128
+    s_v = n_v * T
+    x = synth.vsa_inputs(23, h, s_t, s_v, s_a)
+    q = np.zeros((s_t + s_v + s_a, h, D), dtype=np.float32)
+    q[:, :, 0] = 1.0
+    k = G.widen(x["k"]).astype(np.float32) * 0.25
+    rows = np.arange(s_t + s_v + s_a)
+    k[:, 0, 0] = 4.0 * (rows // T)  # exact in bfloat16
+    x["q"], x["k"] = synth.f32_to_bf16_bits(q), synth.f32_to_bf16_bits(k)
+    assert bsv.vsa_topk_count(s_v, 0.2) == 4
+    ref, e, _, sel, _ = full_check(x, s_t, s_v, s_a, 0.2, exempt_ok=False)
+    assert np.array_equal(sel[0, 0], np.arange(n_v - 4, n_v))
+    # the dense rows' weights really span the parts: the last key tile
+    # carries most of each dense row's softmax mass, the first parts little
+    c2 = np.log2(np.e) / np.sqrt(D)
+    assert 4.0 * (s_t + s_v + s_a - T) / T * c2 > 10
+    print(e)
+
+
 def test_fine_stage_on_oracle_selection():
     """The fine stage honours the index sets it is given: run it on the
     oracle's own selection (and on a shifted one) and compare."""
