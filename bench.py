@@ -353,8 +353,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus > 1 or world > 1:
-        print("bench.py: this build measures one GPU only (the VSA path shards by heads with no "
-              "exchange inside it; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py: measures one GPU only (the VSA path shards by heads, with no "
+              "exchange inside it, so one GPU's share is the whole measurement). "
+              "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
