@@ -386,6 +386,13 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
                     for (int s8 = 0; s8 < 8; ++s8) qf[qb][s8] = z8;
         }
 
+        // Q fragments live in AGPRs (the MFMA reads its B operand from either
+        // register file), which leaves the vector registers to the values that
+        // change every step
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) asm volatile("" : "=a"(qf[qb][s8]) : "0"(qf[qb][s8]));
         const int t0 = tile_at(0), t1 = tile_at(1);
 
         // Softmax reference.  Each column uses one fixed reference m_ref (in units
