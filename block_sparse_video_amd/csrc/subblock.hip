@@ -132,8 +132,9 @@ __device__ __forceinline__ double pair_lse(const f64x4& acc) {
 // grid (H * ceil(n_c / RT)), 512 threads = 8 wavefronts.  A workgroup owns
 // RT groups of four query tiles of one head (4 RT rows of scores in LDS).
 // Wavefront wv multiplies query group wv % RT against the key groups c with
-// c % (8 / RT) == wv / RT, two key groups per step (two independent MFMA
-// chains), and stores the scores; then each wavefront selects rows wv, wv + 8.
+// c % (8 / RT) == wv / RT, four key groups per step (four independent MFMA
+// chains; two, then one, for the remainder), and stores the scores; then
+// each wavefront selects rows wv, wv + 8.
 // Blocks are mapped so that each XCD walks a contiguous, head-major range of
 // (head, query block) items: the key means of one head (n_c * 8 KiB) stay in
 // that XCD's L2 while its CUs share them.
@@ -177,6 +178,29 @@ __global__ __launch_bounds__(512) void subblock_route_kernel(const float* __rest
             if (store_lane && w < n_v) sc[lrow * ldw + w] = s + 0.0;
         };
         int c = ph;
+        for (; c + 3 * PH < n_c; c += 4 * PH) {
+            float bq[4][32];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                load_group(kh + (int64_t)(c + gq * PH) * 2048, lane, lane & 15, bq[gq]);
+                if (4 * (c + gq * PH) + ((lane & 15) >> 2) >= n_v) {
+#pragma unroll
+                    for (int s = 0; s < 32; ++s) bq[gq][s] = 0.0f;
+                }
+            }
+            f64x4 accq[4];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) accq[gq] = (f64x4){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+            for (int s = 0; s < 32; ++s) {
+                const double as = (double)a[s];
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    accq[gq] = __builtin_amdgcn_mfma_f64_16x16x4f64(as, (double)bq[gq][s], accq[gq], 0, 0, 0);
+            }
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) finish(accq[gq], c + gq * PH);
+        }
         for (; c + PH < n_c; c += 2 * PH) {
             float b0[32], b1[32];
             load_group(kh + (int64_t)c * 2048, lane, lane & 15, b0);
