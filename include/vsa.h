@@ -101,9 +101,12 @@ size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_le
  *   offsets[3] coarse     float32 [H][n_v][128]
  *   offsets[4] packed K   bfloat16, 16 KiB per (head, tile), in MFMA operand order
  *   offsets[5] packed V   bfloat16, 16 KiB per (head, tile), in MFMA operand order
- *   offsets[6] total bytes (= vsa_workspace_bytes); the last 1 KiB before it
- *              holds the fine stage's work-queue counters, which every call
- *              clears before use
+ *   offsets[6] total bytes (= vsa_workspace_bytes).  Between packed V and
+ *              the total lie the partial results of text/audio query tiles
+ *              whose key list the fine stage splits into parts (float32,
+ *              33,280 bytes per part, up to 4 parts per tile; none without
+ *              video tiles) and, in the last 1 KiB, the fine stage's
+ *              work-queue counters, which every call clears before use
  * Returns VSA_OK or a shape error.  Host only. */
 vsa_status vsa_workspace_layout(int32_t num_heads, int64_t text_len, int64_t video_len,
                                 int64_t audio_len, size_t offsets[7]);
