@@ -80,12 +80,13 @@ struct FineArgs {
 //    last-level cache, and the resident units of a head start together and
 //    sweep their ascending key lists at the same pace.  With an odd head
 //    count the video units are dealt round-robin to all eight queues;
-//  - then a contiguous, head-major 1/8 share of the dense (text/audio query)
-//    units (N key tiles each, ~4.5x a video unit), so the dense units of one
-//    head share one L2.  They start together once the video units are done
-//    and sweep every tile of their heads in step.  (Dense units first leaves
-//    no long units for the end, but measured 15-20% slower: the video units
-//    then start unevenly and lose their lockstep.)
+//  - then a contiguous 1/8 share of the dense (text/audio query) items,
+//    ordered by head, then key-list part, then query tile.  A dense unit's
+//    list is every tile (~4.5x a video unit's), so it is walked as P parts
+//    of about a video unit's length and the parts are combined afterwards;
+//    the parts of one head share one L2 and sweep their key ranges in step.
+//    (Dense items first measured 15-20% slower: the video units then start
+//    unevenly and lose their lockstep.)
 __device__ __forceinline__ int dense_begin(int D, int x) { return (int)(((int64_t)D * x) / kQueues); }
 
 __device__ __forceinline__ int video_count(int H, int n_v, int x) {
