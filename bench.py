@@ -10,8 +10,8 @@ over synthetic seeded inputs already resident in HBM.  Default workload: the
 Prints ONE JSON line.  value = effective TFLOP/s on computed tiles only
 (QK^T and PV of every computed 64x64 tile pair, 4*64*64*128 FLOP each);
 ms_per_step = ms per layer.  A 14-head run of the same shape (heads 0-13 of
-the same tensors, one SP4 rank's share) is reported under "secondary", and
-the whole attention layer (Q/K/V/gate projections of smooth-field hidden
+the same tensors, one SP4 rank's share) is reported under "secondary", the
+5-second shape at 14 heads under "c1_5s_14h", and the whole attention layer (Q/K/V/gate projections of smooth-field hidden
 states, then the VSA forward) under "full_layer".
 """
 from __future__ import annotations
@@ -446,6 +446,23 @@ def main():
                                "fine_attn_ms": r14["stage_ms"][2],
                                "fine_frac": f14 / (r14["stage_ms"][2] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         del x14, r14
+    if not args.no_secondary and args.workload == "10s_56h":
+        # the 5 s shape at one four-way head split's share (14 heads): its own
+        # seeded inputs, the same timing as the headline
+        h5, t5, v5, a5 = WORKLOADS["5s_14h"]
+        x5, _ = make_inputs("5s_14h", threads)
+        xd5 = {n: to_dev(a, np, torch) for n, a in x5.items()}
+        del x5
+        r5 = time_path(bsv, torch, xd5, (h5, t5, v5, a5), frac, args.steps, args.warmup)
+        k5 = bsv.vsa_topk_count(v5, frac)
+        f5 = tile_pairs(h5, t5, v5, a5, k5) * FLOP_PER_PAIR
+        result["c1_5s_14h"] = {"workload": f"5s_14h: {h5} heads, text {t5} + video {v5} + audio "
+                                           f"{a5} tokens, k={k5}",
+                               "ms_per_step": r5["ms"], "forward_entry_ms": r5["forward_ms"],
+                               "value": f5 / (r5["ms"] * 1e-3) / 1e12,
+                               "stage_ms": r5["stage_ms"],
+                               "fine_frac": f5 / (r5["stage_ms"][2] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del xd5, r5
     if not args.no_subblock and args.workload == "10s_56h":
         result["subblock"] = subblock_leg(bsv, torch, xd, shape, args.steps, args.warmup)
     if not args.no_full_layer and args.workload == "10s_56h":

@@ -43,26 +43,47 @@ def _check(status: int, where: str):
 
 
 def _tensor(t, name, dtype, shape=None):
+    """Check one tensor argument's type, dtype, shape and layout (None passes
+    through).  Every wrapper checks all its arguments this way, then calls
+    _on_gpu on them, before anything reaches the library."""
     torch = _torch()
     if t is None:
         return None
-    if not isinstance(t, torch.Tensor) or not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _on_gpu(**tensors):
+    """Every given tensor must be device memory: a host pointer handed to a
+    kernel would fault the GPU."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise TypeError(f"{name} must be a CUDA (HIP) torch tensor")
+
+
+def _selection(t, num_heads, video_len, k, name="selected_tiles"):
+    """selected_tiles is int32 [H][n_v][k].  When k is not a valid count the
+    shape is left to the library, which returns the matching status."""
+    torch = _torch()
+    if k is None or k < 0:
+        return _tensor(t, name, torch.int32)
+    return _tensor(t, name, torch.int32, (num_heads, video_len // TILE, k))
 
 
 def vsa_topk_count(video_len: int, topk_frac: float) -> int:
     return int(load().vsa_topk_count(video_len, topk_frac))
 
 
-def vsa_workspace_bytes(num_heads: int, text_len: int, video_len: int, audio_len: int) -> int:
-    return int(load().vsa_workspace_bytes(num_heads, text_len, video_len, audio_len))
+def vsa_workspace_bytes(num_heads: int, text_len: int, video_len: int, audio_len: int,
+                        topk_frac: float = 0.2) -> int:
+    return int(load().vsa_workspace_bytes(num_heads, text_len, video_len, audio_len, topk_frac))
 
 
 def vsa_workspace_layout(num_heads: int, text_len: int, video_len: int, audio_len: int) -> dict:
@@ -74,6 +95,10 @@ def vsa_workspace_layout(num_heads: int, text_len: int, video_len: int, audio_le
 
 
 def _shape_args(q, text_len, video_len, audio_len):
+    """Expected [S, H, 128] of the token tensors; H is read from q."""
+    torch = _torch()
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a [S, H, 128] tensor")
     s = text_len + video_len + audio_len
     return (s, q.shape[1], HEAD_DIM)
 
@@ -85,9 +110,11 @@ def vsa_forward(q, k, v, gate, text_len, video_len, audio_len, topk_frac, out, s
     q, k, v, out = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k"), (v, "v"),
                                                                     (out, "out")))
     gate = _tensor(gate, "gate", torch.bfloat16, shp)
-    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32)
+    selected_tiles = _selection(selected_tiles, shp[1], video_len,
+                                vsa_topk_count(video_len, topk_frac))
     workspace = _tensor(workspace, "workspace", torch.uint8)
     nbytes = workspace.numel() if workspace is not None else 0
+    _on_gpu(q=q, k=k, v=v, gate=gate, out=out, selected_tiles=selected_tiles, workspace=workspace)
     _check(load().vsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), shp[1], text_len, video_len,
                               audio_len, topk_frac, _ptr(out), _ptr(selected_tiles), _ptr(workspace),
                               nbytes, _stream(stream)), "vsa_forward")
@@ -98,6 +125,9 @@ def vsa_pool_pack(q, k, v, text_len, video_len, audio_len, workspace, stream=Non
     shp = _shape_args(q, text_len, video_len, audio_len)
     q, k, v = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k"), (v, "v")))
     workspace = _tensor(workspace, "workspace", torch.uint8)
+    if workspace is None:
+        raise ValueError("vsa_pool_pack needs a workspace")
+    _on_gpu(q=q, k=k, v=v, workspace=workspace)
     _check(load().vsa_pool_pack(_ptr(q), _ptr(k), _ptr(v), shp[1], text_len, video_len, audio_len,
                                 _ptr(workspace), workspace.numel(), _stream(stream)),
            "vsa_pool_pack")
@@ -106,8 +136,12 @@ def vsa_pool_pack(q, k, v, text_len, video_len, audio_len, workspace, stream=Non
 def vsa_select_coarse(num_heads, text_len, video_len, audio_len, topk_frac, selected_tiles,
                       workspace, stream=None):
     torch = _torch()
-    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32)
+    selected_tiles = _selection(selected_tiles, num_heads, video_len,
+                                vsa_topk_count(video_len, topk_frac))
     workspace = _tensor(workspace, "workspace", torch.uint8)
+    if workspace is None:
+        raise ValueError("vsa_select_coarse needs a workspace")
+    _on_gpu(selected_tiles=selected_tiles, workspace=workspace)
     _check(load().vsa_select_coarse(num_heads, text_len, video_len, audio_len, topk_frac,
                                     _ptr(selected_tiles), _ptr(workspace), workspace.numel(),
                                     _stream(stream)), "vsa_select_coarse")
@@ -119,8 +153,12 @@ def vsa_fine_attention(q, gate, text_len, video_len, audio_len, topk_frac, selec
     shp = _shape_args(q, text_len, video_len, audio_len)
     q, out = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (out, "out")))
     gate = _tensor(gate, "gate", torch.bfloat16, shp)
-    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32)
+    selected_tiles = _selection(selected_tiles, shp[1], video_len,
+                                vsa_topk_count(video_len, topk_frac))
     workspace = _tensor(workspace, "workspace", torch.uint8)
+    if workspace is None:
+        raise ValueError("vsa_fine_attention needs a workspace")
+    _on_gpu(q=q, gate=gate, out=out, selected_tiles=selected_tiles, workspace=workspace)
     _check(load().vsa_fine_attention(_ptr(q), _ptr(gate), shp[1], text_len, video_len,
                                      audio_len, topk_frac, _ptr(selected_tiles), _ptr(out),
                                      _ptr(workspace), workspace.numel(), _stream(stream)),
@@ -138,7 +176,7 @@ def alloc_outputs(num_heads, text_len, video_len, audio_len, topk_frac, device=N
     n_v = video_len // TILE
     out = torch.empty((s, num_heads, HEAD_DIM), dtype=torch.bfloat16, device=device)
     sel = torch.empty((num_heads, n_v, kk), dtype=torch.int32, device=device)
-    wsb = vsa_workspace_bytes(num_heads, text_len, video_len, audio_len)
+    wsb = vsa_workspace_bytes(num_heads, text_len, video_len, audio_len, topk_frac)
     if wsb == 0:
         raise ValueError("bad shape")
     ws = torch.empty(wsb, dtype=torch.uint8, device=device)
@@ -167,6 +205,7 @@ def vsa_project_qkvg(x, w, num_heads, q, k, v, gate, stream=None):
     w = _tensor(w, "w", torch.bfloat16, (4, num_heads * HEAD_DIM, hidden))
     outs = [_tensor(t, n, torch.bfloat16, (tokens, num_heads, HEAD_DIM))
             for t, n in ((q, "q"), (k, "k"), (v, "v"), (gate, "gate"))]
+    _on_gpu(x=x, w=w, q=outs[0], k=outs[1], v=outs[2], gate=outs[3])
     _check(load().vsa_project_qkvg(_ptr(x), _ptr(w), tokens, hidden, num_heads,
                                    *[_ptr(t) for t in outs], _stream(stream)),
            "vsa_project_qkvg")
@@ -194,14 +233,23 @@ def vsa_forward_padded(q, k, v, gate, text_len, video_len, audio_len, valid, top
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (out, "out")):
         _tensor(t, n, torch.bfloat16, shp)
     _tensor(gate, "gate", torch.bfloat16, shp)
-    if selected_tiles is not None:
-        _tensor(selected_tiles, "selected_tiles", torch.int32)
+    selected_tiles = _selection(selected_tiles, shp[1], video_len,
+                                vsa_topk_count(video_len, topk_frac))
+    workspace = _tensor(workspace, "workspace", torch.uint8)
+    if len(valid) != 3:
+        raise ValueError("valid must be (text, video, audio) token rows")
     g6 = None
     if gamma_q is not None or gamma_k is not None:
         _tensor(gamma_q, "gamma_q", torch.bfloat16, (shp[1], HEAD_DIM))
         _tensor(gamma_k, "gamma_k", torch.bfloat16, (shp[1], HEAD_DIM))
         _tensor(q_out, "q_out", torch.bfloat16, shp)
+        if gamma_q is None or gamma_k is None or q_out is None or grid is None:
+            raise ValueError("gamma_q, gamma_k, q_out and grid go together")
+        if len(grid) != 3 or len(tile) != 3:
+            raise ValueError("grid and tile are (T, H, W) triples")
         g6 = (ctypes.c_int32 * 6)(*grid, *tile)
+    _on_gpu(q=q, k=k, v=v, gate=gate, out=out, selected_tiles=selected_tiles,
+            workspace=workspace, gamma_q=gamma_q, gamma_k=gamma_k, q_out=q_out)
     _check(load().vsa_forward_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(gamma_q),
                                      _ptr(gamma_k), g6, shp[1], text_len, video_len, audio_len,
                                      valid[0], valid[1], valid[2], topk_frac, _ptr(q_out),
@@ -232,9 +280,11 @@ def vsa_forward_subblock(q, k, v, text_len, video_len, audio_len, sparsity, out,
     shp = _shape_args(q, text_len, video_len, audio_len)
     q, k, v, out = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k"), (v, "v"),
                                                                     (out, "out")))
-    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32)
+    selected_tiles = _selection(selected_tiles, shp[1], video_len,
+                                vsa_subblock_count(video_len, sparsity))
     workspace = _tensor(workspace, "workspace", torch.uint8)
     nbytes = workspace.numel() if workspace is not None else 0
+    _on_gpu(q=q, k=k, v=v, out=out, selected_tiles=selected_tiles, workspace=workspace)
     _check(load().vsa_forward_subblock(_ptr(q), _ptr(k), _ptr(v), shp[1], text_len, video_len,
                                        audio_len, sparsity, _ptr(out), _ptr(selected_tiles),
                                        _ptr(workspace), nbytes, _stream(stream)),
@@ -246,8 +296,12 @@ def vsa_subblock_select(q, k, text_len, video_len, audio_len, sparsity, selected
     torch = _torch()
     shp = _shape_args(q, text_len, video_len, audio_len)
     q, k = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k")))
-    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32)
+    selected_tiles = _selection(selected_tiles, shp[1], video_len,
+                                vsa_subblock_count(video_len, sparsity))
     workspace = _tensor(workspace, "workspace", torch.uint8)
+    if workspace is None:
+        raise ValueError("vsa_subblock_select needs a workspace")
+    _on_gpu(q=q, k=k, selected_tiles=selected_tiles, workspace=workspace)
     _check(load().vsa_subblock_select(_ptr(q), _ptr(k), shp[1], text_len, video_len, audio_len,
                                       sparsity, _ptr(selected_tiles), _ptr(workspace),
                                       workspace.numel(), _stream(stream)), "vsa_subblock_select")

@@ -18,7 +18,7 @@ _SZ = ctypes.c_size_t
 SIGNATURES = {
     "vsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "vsa_topk_count": (_I32, [_I64, _F32]),
-    "vsa_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64]),
+    "vsa_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _F32]),
     "vsa_workspace_layout": (ctypes.c_int, [_I32, _I64, _I64, _I64, ctypes.POINTER(_SZ)]),
     "vsa_forward": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _F32, _P, _P, _P, _SZ, _P]),
     "vsa_pool_pack": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I64, _I64, _P, _SZ, _P]),

@@ -65,6 +65,7 @@ struct FineArgs {
     uint32_t* sched;    // kQueues work-queue counters, 32 words apart, zero at launch
     float* partial;     // dense parts: [dense unit][part][64 x 128 O, 64 l, 64 reference]
     int parts;          // key-list parts per dense unit (1: no split)
+    int check_sel;      // nonzero: validate each selection row before use (caller-supplied rows)
     int H, n_t, n_v, n_a, N, kk;
     int last_valid[3];  // token rows in the last text / video / audio tile (64 when full)
     float scale_log2;   // log2(e) / sqrt(128)
@@ -194,6 +195,24 @@ __device__ __forceinline__ float xhalf_sum(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                     false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A selection row is usable when it holds kk distinct video tiles in
+// ascending order, each in [0, n_v).  Checked by the whole wavefront, 64
+// entries at a time; ordinary vector loads, issued before the unit starts
+// its own copies.
+__device__ __forceinline__ bool selection_row_ok(const int32_t* row, int kk, int n_v, int lane) {
+    bool bad = false;
+#pragma unroll 1
+    for (int i0 = 0; i0 < kk; i0 += 64) {
+        const int i = i0 + lane;
+        if (i < kk) {
+            const int w = row[i];
+            const int prev = i > 0 ? row[i - 1] : -1;
+            bad = bad || w < 0 || w >= n_v || w <= prev;
+        }
+    }
+    return __ballot(bad) == 0;
 }
 
 // Scalar (wave-uniform) load of one selected-tile index: a scalar load keeps
@@ -334,6 +353,17 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
             video ? a.n_t + a.kk + a.n_a : (int)((int64_t)(part + 1) * a.N / a.parts) - it0;
         const int32_t* selrow = a.sel + ((int64_t)h * a.n_v + (video ? u : 0)) * a.kk;
         const float c2 = a.scale_log2;
+        if (a.check_sel && video && !selection_row_ok(selrow, a.kk, a.n_v, lane)) {
+            // a malformed row is not attended: the unit's 64 output rows are
+            // written as NaN, so the error cannot pass for a result
+            const uint4 nan8 = make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int row = (lane >> 4) + 4 * i;
+                *(uint4*)(a.out + ((int64_t)j * kT + row) * rs + (int64_t)h * kD + 8 * (lane & 15)) = nan8;
+            }
+            continue;
+        }
 
         // position `it` of this unit's ascending key-tile list -> tile index;
         // positions past the end name the last tile
@@ -342,7 +372,8 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
             if (!video) return it0 + it;
             if (it < a.n_t) return it;
             if (it < a.n_t + a.kk) {
-                // caller-supplied index sets are clamped into range, never followed out of bounds
+                // rows are validated (caller-supplied) or valid by construction;
+                // the clamp only keeps every address inside the packed tiles
                 const int w = load_uniform(selrow + (it - a.n_t));
                 return a.n_t + (w < 0 ? 0 : (w >= a.n_v ? a.n_v - 1 : w));
             }
@@ -711,7 +742,7 @@ int fine_slots() {
 
 hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate, const int32_t* sel,
                                  uint16_t* out, const Shape& s, uint8_t* ws, const Layout& L,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, bool check_sel) {
     FineArgs a;
     a.q = q;
     a.gate = gate;
@@ -723,6 +754,7 @@ hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate, const 
     a.sched = (uint32_t*)(ws + L.sched);
     a.partial = (float*)(ws + L.partial);
     a.parts = dense_parts(s);
+    a.check_sel = check_sel ? 1 : 0;
     a.H = s.H;
     a.n_t = s.n_t;
     a.n_v = s.n_v;

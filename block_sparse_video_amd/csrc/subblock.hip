@@ -1,11 +1,12 @@
 // subblock.hip -- the SubBlock router on gfx950: a second tile-selection rule
 // whose selection feeds the same fine attention kernel.
 //
-// The SGLang Diffusion benchmark page, section "How SubBlock Sparse Attention
-// Works": every 64-token query and key block is split into four 16-token
-// sub-blocks; a pooled log-sum-exp score estimates, per head and query block,
-// the unnormalised softmax mass of each key block; the highest-scoring key
-// blocks are kept, the kept count rounded to whole groups of 8 blocks.
+// Router of the SGLang Diffusion benchmark page, section "How SubBlock Sparse
+// Attention Works", restated: query and key tiles of 64 tokens are each cut
+// into four 16-token pieces; one number per (head, query tile, key tile),
+// built from the means of the pieces with a log-sum-exp, estimates the key
+// tile's unnormalised softmax weight for that query tile, and each query tile
+// keeps its highest-scoring key tiles, the count a whole multiple of 8.
 // Definitions used (head h, video query tile u, video key tile w):
 //   Qs[u][a], Ks[w][b] = float32 means of the 16 rows of sub-block a (b),
 //                        summed in float64 (exact for bfloat16 inputs)

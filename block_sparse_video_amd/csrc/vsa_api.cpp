@@ -150,9 +150,11 @@ int32_t vsa_topk_count(int64_t video_len, float topk_frac) {
     return topk_count(video_len / VSA_TILE, topk_frac);
 }
 
-size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_len, int64_t audio_len) {
+size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_len, int64_t audio_len,
+                           float topk_frac) {
     Shape s;
     if (make_shape(num_heads, text_len, video_len, audio_len, &s) != VSA_OK) return 0;
+    if (check_topk(topk_frac, &s) != VSA_OK) return 0;
     return vsa::make_layout(s).total;
 }
 
@@ -221,8 +223,10 @@ vsa_status vsa_fine_attention(const void* q, const void* gate, int32_t num_heads
     const Layout L = vsa::make_layout(s);
     if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
     if ((st = check_device()) != VSA_OK) return st;
-    return from_hip(vsa::launch_fine_attention((const uint16_t*)q, (const uint16_t*)gate, selected_tiles, (uint16_t*)out,
-                                               s, (uint8_t*)workspace, L, (hipStream_t)stream));
+    return from_hip(vsa::launch_fine_attention((const uint16_t*)q, (const uint16_t*)gate,
+                                               selected_tiles, (uint16_t*)out, s,
+                                               (uint8_t*)workspace, L, (hipStream_t)stream,
+                                               /*check_sel=*/true));
 }
 
 vsa_status vsa_forward(const void* q, const void* k, const void* v, const void* gate,

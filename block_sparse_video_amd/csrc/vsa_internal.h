@@ -119,9 +119,12 @@ hipError_t launch_pool_pack(const uint16_t* q, const uint16_t* k, const uint16_t
                             const Prep* prep = nullptr, uint16_t* q_out = nullptr);
 hipError_t launch_select_coarse(const Shape& s, int32_t* sel, uint8_t* ws, const Layout& L,
                                 hipStream_t stream);
+// check_sel: validate every selection row on the device first (rows given by
+// the caller); a malformed row's 64 output rows are written as NaN.
 hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate,
                                  const int32_t* sel, uint16_t* out, const Shape& s,
-                                 uint8_t* ws, const Layout& L, hipStream_t stream);
+                                 uint8_t* ws, const Layout& L, hipStream_t stream,
+                                 bool check_sel = false);
 
 // SubBlock router: sub-block means of Q and K, scores and top-k (s.k tiles).
 hipError_t launch_subblock_route(const uint16_t* q, const uint16_t* k, const Shape& s,

@@ -91,8 +91,10 @@ const char* vsa_status_string(vsa_status s);
 int32_t vsa_topk_count(int64_t video_len, float topk_frac);
 
 /* Workspace bytes needed by vsa_forward and the stage calls below for this
- * shape; 0 if the shape is invalid.  Host only. */
-size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_len, int64_t audio_len);
+ * shape and top-k fraction; 0 if the shape or topk_frac is invalid (the
+ * same checks as vsa_forward).  Host only. */
+size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_len, int64_t audio_len,
+                           float topk_frac);
 
 /* Byte offsets of the workspace regions, for inspection by tests:
  *   offsets[0] pooled Q   float64 [H][n_v][128] (the FP32 statistic, widened)
@@ -139,10 +141,15 @@ vsa_status vsa_select_coarse(int32_t num_heads, int64_t text_len, int64_t video_
 
 /* Stage 3 (sections "The FastH3 workload" and "Fused output combination"):
  * fine block-sparse attention of every query tile over its key tiles, with
- * the gated coarse term added in the epilogue.  selected_tiles may be any
- * [H][n_v][k] array of video tile indices (k from topk_frac); indices
- * outside [0, n_v) are clamped into it, a repeated index is attended twice,
- * and ascending order is not required.
+ * the gated coarse term added in the epilogue.  selected_tiles is any
+ * [H][n_v][k] array of video tile indices (k from topk_frac) whose rows each
+ * hold k distinct indices in [0, n_v), ascending.  Every row is checked on
+ * the device before it is used: a row that breaks this (an index out of
+ * range, repeated or out of order) is not attended, and the 64 output rows
+ * of that (head, video query tile) are written as NaN, so a malformed
+ * selection shows as NaN rather than as a plausible result.  The call itself
+ * still returns VSA_OK (the rows live on the device); other rows are
+ * computed normally.
  * Reads the packed K and V tiles and the coarse output that stages 1 and 2
  * left in the workspace.  workspace is required. */
 vsa_status vsa_fine_attention(const void* q, const void* gate, int32_t num_heads,

@@ -3,7 +3,9 @@
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The GPU library never uses it.
 
-Thin ctypes binding over ``vsa_oracle.c`` (plain C, float64).  Arrays are
+Thin ctypes binding over ``vsa_oracle.c`` (plain C, float64 arithmetic;
+tile means are rounded once to FP32, the pooled-statistics precision the page
+fixes).  Arrays are
 numpy: bfloat16 tensors travel as ``uint16`` bit patterns, token-major
 ``[S, H, 128]``.  The method follows the page "UniServe: serving FastH3 at its
 fastest" (sections "The FastH3 workload", "Fused attention preprocessing",

@@ -21,7 +21,11 @@
  * (0 <= u < n_v) holds tokens S_t + 64u .. S_t + 64u + 63.
  *
  * Every value below is computed in float64 unless stated otherwise.  A
- * bfloat16 input widens to float64 exactly.
+ * bfloat16 input widens to float64 exactly.  The one stated exception: a
+ * tile mean (and a SubBlock piece mean) is rounded once to float32 after its
+ * float64 sum is divided by the row count, because the page fixes the pooled
+ * statistics as FP32; the scores are then float64 dot products of those
+ * float32 means.
  *
  * Parity pins (tests under tests/, marked "not gpu"): brute-force masked
  * dense attention on tiny inputs, topk_frac = 1 against the textbook dense
@@ -499,20 +503,27 @@ int32_t vsa_oracle_default_threads(void) { return resolve_threads(0); }
 /* ------------------------------------------------------------------------ */
 
 /* The SGLang Diffusion benchmark page, section "How SubBlock Sparse
- * Attention Works": 64-token query and key blocks are split into four
- * 16-token sub-blocks on both sides; a pooled log-sum-exp score estimates
- * each key block's unnormalised softmax mass for each query block and head;
- * the highest-scoring key blocks are kept.  The sparsity is the fraction of
- * blocks dropped, and the kept count is rounded to whole groups of 8 blocks.
- * Readings: the sub-block statistics are FP32 means of 16 rows (as the tile
+ * Attention Works", describes this router.  Restated: on both the query and
+ * the key side a 64-token tile is cut into four 16-token pieces; for one
+ * head, the pull of key tile w on query tile u is summarised by a single
+ * number, the log of the summed exponentials of the 16 scaled dot products
+ * between piece means, which stands in for the unnormalised softmax weight
+ * the key tile would receive.  Each query tile keeps the key tiles with the
+ * largest such numbers; `sparsity` is the share of candidate tiles dropped
+ * and the number kept is a whole multiple of 8.
+ * Readings: the piece statistics are FP32 means of 16 rows (as the tile
  * means above); the score of key tile w for query tile u is
  *   score(u, w) = log sum_{a, b < 4} exp(alpha * qsub[u][a] . ksub[w][b]),
  * alpha = 1/sqrt(128), dots as in pooled_score; the kept count is
- *   k = 8 * floor((1 - sparsity) * n_v / 8 + 1/2), clamped to [min(8, n_v), n_v];
- * ties go to the lower tile index (as the main rule).  In this path the
- * router ranks the video key tiles of each video query tile; text and audio
- * keys stay dense and there is no coarse term, so the fine branch is reused
- * as it is. */
+ *   k = 8 * floor((1 - sparsity) * n / 8 + 1/2), clamped to [min(8, n), n]
+ * for n candidate tiles; ties go to the lower tile index (as the main rule).
+ * Two candidate sets are offered.  Video mode: the router ranks the video
+ * key tiles of each video query tile (n = n_v); text and audio keys stay
+ * dense and text/audio queries attend to everything, so the main path's
+ * fine branch is reused as it is.  Whole-sequence mode, the page's own
+ * reading: every query tile of the joint sequence (text, video and audio)
+ * ranks every key tile of the sequence (n = N) and attends to its kept
+ * tiles only.  Neither mode has a coarse term. */
 int32_t vsa_oracle_subblock_count(int64_t n_v, double sparsity) {
     if (!(sparsity >= 0.0 && sparsity < 1.0) || n_v < 0) return -1;
     if (n_v == 0) return 0;

@@ -186,3 +186,55 @@ def test_subblock_select_validation():
     assert f(FAKE, FAKE, 2, 64, 640, 64, 0.75, FAKE, None, 1 << 40, None) == WORKSPACE
     assert f(FAKE, FAKE, 2, 64, 640, 64, 0.75, FAKE, FAKE, 64, None) == WORKSPACE
     assert f(FAKE, FAKE, 2, 64, 64 * 6000, 64, 0.75, FAKE, FAKE, 1 << 40, None) == TOO_LARGE
+
+
+def padded(**kw):
+    """vsa_forward_padded with fake device pointers: every case below fails
+    validation before the library touches the GPU."""
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gq=None, gk=None, grid=None, h=2, t=128, vid=640,
+             au=128, tv=100, vv=600, av=65, frac=0.2, qo=None, out=FAKE, sel=FAKE, ws=FAKE,
+             wsb=1 << 40)
+    a.update(kw)
+    grid = None if a["grid"] is None else (ctypes.c_int32 * 6)(*a["grid"])
+    return _native.load().vsa_forward_padded(
+        a["q"], a["k"], a["v"], a["g"], a["gq"], a["gk"], grid, a["h"], a["t"], a["vid"], a["au"],
+        a["tv"], a["vv"], a["av"], a["frac"], a["qo"], a["out"], a["sel"], a["ws"], a["wsb"], None)
+
+
+PREP = dict(gq=FAKE, gk=FAKE, qo=FAKE, grid=(2, 10, 30, 1, 2, 2))  # 2*10*30 = 600 video tokens
+
+
+@pytest.mark.parametrize("kw,code", [
+    # required pointers
+    (dict(q=None), NULLP), (dict(k=None), NULLP), (dict(v=None), NULLP), (dict(out=None), NULLP),
+    (dict(g=None), NULLP), (dict(sel=None), NULLP),
+    # preprocessing arguments come together: both gammas, q_out and grid
+    (dict(PREP, gk=None), NULLP), (dict(PREP, gq=None), NULLP), (dict(PREP, qo=None), NULLP),
+    (dict(PREP, grid=None), NULLP),
+    # shape
+    (dict(h=0), SHAPE), (dict(t=-64), SHAPE), (dict(vid=100), UNALIGNED),
+    # valid rows: only a segment's last tile may be padding, and none of an empty segment
+    (dict(tv=129), SHAPE), (dict(tv=64), SHAPE), (dict(tv=0), SHAPE),
+    (dict(vv=641), SHAPE), (dict(vv=576), SHAPE), (dict(av=-1), SHAPE), (dict(av=64), SHAPE),
+    (dict(t=0, tv=1), SHAPE), (dict(au=0, av=5), SHAPE),
+    # the latent grid: positive, divisible by the tile, T*H*W = video_valid
+    (dict(PREP, grid=(0, 10, 30, 1, 2, 2)), SHAPE), (dict(PREP, grid=(2, 10, 30, 1, 0, 2)), SHAPE),
+    (dict(PREP, grid=(2, 10, 30, 1, 3, 2)), SHAPE), (dict(PREP, grid=(2, 10, 30, 2, 2, 4)), SHAPE),
+    (dict(PREP, grid=(2, 10, 31, 1, 2, 1)), SHAPE),
+    # top-k fraction
+    (dict(frac=0.0), TOPK), (dict(frac=1.5), TOPK),
+    # alignment of every pointer, gammas and q_out included
+    (dict(q=FAKE + 2), MISALIGNED), (dict(out=FAKE + 8), MISALIGNED),
+    (dict(sel=FAKE + 4), MISALIGNED), (dict(PREP, qo=FAKE + 2), MISALIGNED),
+    (dict(PREP, gq=FAKE + 8), MISALIGNED), (dict(PREP, gk=FAKE + 4), MISALIGNED),
+    (dict(ws=FAKE + 16), MISALIGNED),
+    # workspace size
+    (dict(wsb=1000), WORKSPACE),
+    (dict(vid=64 * 20000, vv=64 * 20000), TOO_LARGE),
+])
+def test_padded_validation(kw, code):
+    assert padded(**kw) == code
+
+
+def test_padded_without_video_allows_null_gate_and_selection():
+    assert padded(vid=0, vv=0, g=None, sel=None, wsb=10) == WORKSPACE

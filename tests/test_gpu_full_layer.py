@@ -106,23 +106,22 @@ def test_full_layer_projection_and_vsa():
     n_exempt = G.check_selection(got_sel, ref)
     wsp = G.read_workspace(ws, h, s_t, s_v, s_a)
     np.testing.assert_allclose(wsp["coarse"], ref["coarse"], rtol=2e-5, atol=2e-7)
+    # Projected Q/K/V have std ~1.5, so outputs reach several units (iid
+    # unit-variance inputs give rms ~0.013): the bf16 rounding of one output
+    # element alone is then up to 2^-8 of it, close to 2e-2 by itself.  The
+    # max-abs bar therefore applies to the error beyond each element's own
+    # output rounding; mean-abs 2e-3 and the relative gate are unchanged.  The
+    # summary prints the magnitudes and whether the flat bar held anyway.
+    cov = G.full_size_coverage({"q": qb, "k": kb, "v": vb, "gate": gb}, out, got_sel,
+                               ref["coarse"], s_t, s_v, s_a, threads=THREADS,
+                               rounding_allowance=True, label="full layer")
     orow = G.sample_rows(s_t, s_v, s_a, n_video_tiles=3, per_tile=(0, 37, 63))
     _, ref_out = oracle.fine(qb, kb, vb, gb, s_t, s_v, s_a, got_sel, ref["coarse"], orow,
                              threads=THREADS)
-    got_out = G.widen(G.from_dev_bits(out)[orow])
-    d = np.abs(got_out - ref_out)
-    rms_ref = float(np.sqrt((ref_out ** 2).mean()))
-    e = {"max_abs": float(d.max()), "mean_abs": float(d.mean()),
-         "rel_rms": float(np.sqrt((d ** 2).mean()) / rms_ref),
-         "ref_rms": rms_ref, "ref_max": float(np.abs(ref_out).max())}
-    # The absolute bars (2e-2, 2e-3) were set for the unit-variance iid inputs,
-    # whose outputs have rms ~0.013.  Projected Q/K/V here have std ~1.5, so the
-    # outputs are ~30x larger; the bars scale with them (bf16 holds about three
-    # significant digits), and the relative RMS gate is unchanged.
-    assert e["rel_rms"] <= G.REL_RMS, e
-    assert e["max_abs"] <= max(G.MAX_ABS, 2.0 ** -6 * e["ref_max"]), e
-    assert e["mean_abs"] <= max(G.MEAN_ABS, 2.0 ** -8 * float(np.abs(ref_out).mean())), e
+    e = G.assert_outputs_close(G.from_dev_bits(out)[orow], ref_out, rounding_allowance=True)
+    e.update(ref_rms=float(np.sqrt((ref_out ** 2).mean())))
     # smooth video fields make neighbouring query tiles choose overlapping key tiles
     s0 = got_sel[0]
     overlap = np.mean([len(np.intersect1d(s0[u], s0[u + 1])) / s0.shape[1] for u in range(0, 1000, 7)])
-    print("exempt rows:", n_exempt, e, "neighbour overlap:", round(float(overlap), 3), flush=True)
+    print("exempt rows:", n_exempt, "sampled rows:", e, "coverage:", cov,
+          "neighbour overlap:", round(float(overlap), 3), flush=True)

@@ -306,6 +306,56 @@ def test_fine_stage_on_oracle_selection():
         G.assert_outputs_close(G.from_dev_bits(out), r)
 
 
+def test_fine_stage_rejects_malformed_rows():
+    """vsa_fine_attention checks every caller-supplied selection row on the
+    device: a row with an index out of range, a repeated index or indices out
+    of order is not attended and its 64 output rows come back as NaN; every
+    other row is computed as usual."""
+    announce("malformed selection rows: h=2 tiles=(1,12,1) k=4")
+    h, s_t, s_v, s_a = 2, 64, 64 * 12, 64
+    x = synth.vsa_inputs(27, h, s_t, s_v, s_a)
+    xd = G.inputs_to_dev(x)
+    ref = oracle.select_coarse(x["q"], x["k"], x["v"], s_t, s_v, s_a, 0.3)
+    assert ref["k"] == 4
+    out, sel, ws = bsv.alloc_outputs(h, s_t, s_v, s_a, 0.3)
+    bsv.vsa_pool_pack(xd["q"], xd["k"], xd["v"], s_t, s_v, s_a, ws)
+    bsv.vsa_select_coarse(h, s_t, s_v, s_a, 0.3, sel, ws)
+    bad_sel = ref["sel"].copy()
+    bad = {(0, 1): [0, 3, 5, 12],     # index == n_v
+           (0, 7): [-1, 2, 3, 4],     # negative index
+           (1, 0): [2, 2, 5, 6],      # repeated
+           (1, 11): [1, 4, 3, 8]}     # out of order
+    for (hh, u), row in bad.items():
+        bad_sel[hh, u] = row
+    seld = torch.from_numpy(np.ascontiguousarray(bad_sel, dtype=np.int32)).cuda()
+    out.fill_(0.0)
+    bsv.vsa_fine_attention(xd["q"], xd["gate"], s_t, s_v, s_a, 0.3, seld, out, ws)
+    torch.cuda.synchronize()
+    o = G.widen(G.from_dev_bits(out))
+    for hh in range(h):
+        for u in range(12):
+            rows = slice(s_t + u * T, s_t + (u + 1) * T)
+            if (hh, u) in bad:
+                assert np.isnan(o[rows, hh]).all(), (hh, u)
+            else:
+                assert np.isfinite(o[rows, hh]).all(), (hh, u)
+    all_rows = np.arange(s_t + s_v + s_a)
+    _, r0 = oracle.fine(x["q"], x["k"], x["v"], x["gate"], s_t, s_v, s_a, ref["sel"],
+                        ref["coarse"], all_rows)
+    got = G.from_dev_bits(out)
+    for hh in range(h):
+        good = [r for r in all_rows
+                if not (s_t <= r < s_t + s_v and (hh, (r - s_t) // T) in bad)]
+        G.assert_outputs_close(got[good, hh], r0[good, hh])
+    # the fused entry point never validates (its selection is its own) and the
+    # same workspace still gives the oracle's result afterwards
+    bsv.vsa_fine_attention(xd["q"], xd["gate"], s_t, s_v, s_a, 0.3, sel, out, ws)
+    torch.cuda.synchronize()
+    _, r1 = oracle.fine(x["q"], x["k"], x["v"], x["gate"], s_t, s_v, s_a, sel.cpu().numpy(),
+                        ref["coarse"], np.arange(s_t + s_v + s_a))
+    G.assert_outputs_close(G.from_dev_bits(out), r1)
+
+
 def test_deterministic_and_head_slice():
     announce("determinism + head slice")
     s_t, s_v, s_a = 64, 64 * 24, 64
@@ -346,7 +396,11 @@ BIG = {
 
 @pytest.mark.slow
 @pytest.mark.parametrize("name", list(BIG))
-def test_full_size_selection_and_sampled_rows(name):
+def test_full_size_selection_and_outputs(name):
+    """Every selection row and coarse vector; the whole output finite; all 64
+    rows of several tiles of 8 heads and one row of every query tile of the
+    first and last head against the oracle (the persistent queues and the
+    split dense parts only run at these sizes)."""
     h, s_t, s_v, s_a = BIG[name]
     announce(f"full size {name}: h={h} ({s_t},{s_v},{s_a}) k={bsv.vsa_topk_count(s_v, 0.2)}")
     x = synth.vsa_inputs(0, h, s_t, s_v, s_a, threads=THREADS)
@@ -357,13 +411,9 @@ def test_full_size_selection_and_sampled_rows(name):
     n_exempt = G.check_selection(got_sel, ref)
     w = G.read_workspace(ws, h, s_t, s_v, s_a)
     np.testing.assert_allclose(w["coarse"], ref["coarse"], rtol=2e-5, atol=2e-7)
-    rows = G.sample_rows(s_t, s_v, s_a, n_video_tiles=3, per_tile=(0, 37, 63))
-    _, ref_out = oracle.fine(x["q"], x["k"], x["v"], x["gate"], s_t, s_v, s_a, got_sel,
-                             ref["coarse"], rows, threads=THREADS)
-    got = G.from_dev_bits(out)[rows]
-    e = G.assert_outputs_close(got, ref_out)
-    assert np.isfinite(G.widen(G.from_dev_bits(out[::997]))).all()
-    print(name, "exempt rows:", n_exempt, e, flush=True)
+    cov = G.full_size_coverage(x, out, got_sel, ref["coarse"], s_t, s_v, s_a, threads=THREADS,
+                               label=name)
+    print(name, "exempt rows:", n_exempt, cov, flush=True)
     del xd, out, ws
     torch.cuda.empty_cache()
 

@@ -238,10 +238,8 @@ def test_full_size_10s_56h_sampled():
     check_rows(gp, ref["sel"], ref["scores"], ref["kth"])
     qs, ks = read_subs(ws, h, s_t, s_v, s_a)
     assert np.array_equal(qs, ref["qsub"]) and np.array_equal(ks, ref["ksub"])
-    rows = G.sample_rows(s_t, s_v, s_a, n_video_tiles=4, per_tile=(0, 63))
-    _, ref_out = oracle.fine(x["q"], x["k"], x["v"], np.zeros_like(x["q"]), s_t, s_v, s_a, got,
-                             np.zeros((h, n_v, D)), rows, threads=THREADS)
-    G.assert_outputs_close(G.from_dev_bits(out)[rows], ref_out)
+    G.full_size_coverage({n: x[n] for n in ("q", "k", "v")}, out, got, None, s_t, s_v, s_a,
+                         threads=THREADS, label="subblock 10s_56h")
 
 
 def test_subblock_graph_capture_replays():

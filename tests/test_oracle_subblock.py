@@ -1,8 +1,10 @@
 """Pins of the oracle's SubBlock router (SGLang Diffusion benchmark page,
-section "How SubBlock Sparse Attention Works"): 64-token blocks split into
-four 16-token sub-blocks on both sides, a pooled log-sum-exp score standing
-for each key block's unnormalised softmax mass, the top blocks kept with the
-kept count rounded to whole groups of 8.
+section "How SubBlock Sparse Attention Works").  The rule, restated: tiles of
+64 tokens are cut into four 16-token pieces on the query and on the key side;
+a log-sum-exp over the 16 scaled dot products of piece means scores each
+(query tile, key tile) pair as an estimate of the key tile's unnormalised
+softmax weight; each query tile keeps its best-scoring key tiles, a whole
+multiple of 8 of them.
 
 The pins do not retype the oracle's loops: the score is checked against the
 exact softmax mass of token-level inputs whose rows are constant inside each
