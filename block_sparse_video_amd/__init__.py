@@ -19,7 +19,8 @@ TILE = 64
 __all__ = ["vsa_topk_count", "vsa_workspace_bytes", "vsa_workspace_layout", "vsa_forward",
            "vsa_pool_pack", "vsa_select_coarse", "vsa_fine_attention", "forward", "VsaError",
            "status_string", "LIB_PATH", "vsa_subblock_count", "vsa_subblock_workspace_bytes",
-           "vsa_forward_subblock", "vsa_subblock_select", "forward_subblock"]
+           "vsa_forward_subblock", "vsa_subblock_select", "forward_subblock",
+           "vsa_forward_noalloc"]
 
 
 def _torch():
@@ -118,6 +119,25 @@ def vsa_forward(q, k, v, gate, text_len, video_len, audio_len, topk_frac, out, s
     _check(load().vsa_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), shp[1], text_len, video_len,
                               audio_len, topk_frac, _ptr(out), _ptr(selected_tiles), _ptr(workspace),
                               nbytes, _stream(stream)), "vsa_forward")
+
+
+def vsa_forward_noalloc(q, k, v, gate, text_len, video_len, audio_len, topk_frac, out,
+                        selected_tiles, stream=None):
+    """vsa_forward with the workspace in the library's fixed device array
+    (VSA_NOALLOC_SCRATCH_BYTES per device): allocates nothing.  Calls that
+    overlap in time on one device race on that array."""
+    torch = _torch()
+    shp = _shape_args(q, text_len, video_len, audio_len)
+    q, k, v, out = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k"), (v, "v"),
+                                                                    (out, "out")))
+    gate = _tensor(gate, "gate", torch.bfloat16, shp)
+    selected_tiles = _selection(selected_tiles, shp[1], video_len,
+                                vsa_topk_count(video_len, topk_frac))
+    _on_gpu(q=q, k=k, v=v, gate=gate, out=out, selected_tiles=selected_tiles)
+    _check(load().vsa_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(gate), shp[1], text_len,
+                                      video_len, audio_len, topk_frac, _ptr(out),
+                                      _ptr(selected_tiles), _stream(stream)),
+           "vsa_forward_noalloc")
 
 
 def vsa_pool_pack(q, k, v, text_len, video_len, audio_len, workspace, stream=None):

@@ -27,6 +27,8 @@ SIGNATURES = {
     "vsa_project_qkvg": (ctypes.c_int, [_P, _P, _I64, _I32, _I32, _P, _P, _P, _P, _P]),
     "vsa_forward_padded": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I32, _I64, _I64, _I64,
                                           _I64, _I64, _I64, _F32, _P, _P, _P, _P, _SZ, _P]),
+    "vsa_forward_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _F32, _P, _P,
+                                           _P]),
     "vsa_subblock_count": (_I32, [_I64, _F32]),
     "vsa_subblock_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64]),
     "vsa_forward_subblock": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I64, _I64, _F32, _P, _P, _P,

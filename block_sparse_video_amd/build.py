@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_PATH = os.path.join(PKG, "libvsa.so")
-SOURCES = ["pool_pack.hip", "select_coarse.hip", "fine_attn.hip", "gemm_qkvg.hip", "subblock.hip", "vsa_api.cpp"]
+SOURCES = ["pool_pack.hip", "select_coarse.hip", "fine_attn.hip", "gemm_qkvg.hip", "subblock.hip",
+           "noalloc.hip", "vsa_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 

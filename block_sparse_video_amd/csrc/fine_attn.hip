@@ -66,7 +66,7 @@ struct FineArgs {
     float* partial;     // dense parts: [dense unit][part][64 x 128 O, 64 l, 64 reference]
     int parts;          // key-list parts per dense unit (1: no split)
     int check_sel;      // nonzero: validate each selection row before use (caller-supplied rows)
-    int H, n_t, n_v, n_a, N, kk;
+    int H, ldh, n_t, n_v, n_a, N, kk;  // ldh: heads per token row (row stride / 128)
     int last_valid[3];  // token rows in the last text / video / audio tile (64 when full)
     float scale_log2;   // log2(e) / sqrt(128)
 };
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         int h, j, part;
         queue_unit(a.H, a.n_t, a.n_v, a.n_a, a.parts, qx, qi, h, j, part);
         if (h >= a.H || j >= a.N) break;  // not reached: the queues partition the units
-        const int64_t rs = (int64_t)a.H * kD;  // elements between consecutive tokens
+        const int64_t rs = (int64_t)a.ldh * kD;  // elements between consecutive tokens
         const bool video = j >= a.n_t && j < a.n_t + a.n_v;
         const int u = j - a.n_t;
         // a dense unit's list (every tile) is walked as `parts` contiguous
@@ -680,7 +680,7 @@ __global__ __launch_bounds__(256) void combine_parts_kernel(FineArgs a) {
     const int h = du / n_h, t = du - h * n_h;
     const int j = t < a.n_t ? t : a.n_v + t;
     const int nq = tile_rows(a, j);
-    const int64_t rs = (int64_t)a.H * kD;
+    const int64_t rs = (int64_t)a.ldh * kD;
     const float* base = a.partial + (int64_t)du * a.parts * kPartFloats;
     const int c = threadIdx.x & 15;
 #pragma unroll 1
@@ -756,6 +756,7 @@ hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate, const 
     a.parts = dense_parts(s);
     a.check_sel = check_sel ? 1 : 0;
     a.H = s.H;
+    a.ldh = s.ldh;
     a.n_t = s.n_t;
     a.n_v = s.n_v;
     a.n_a = s.n_a;

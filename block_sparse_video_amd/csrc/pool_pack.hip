@@ -25,7 +25,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // heads x 16 column chunks of 8 dims; each thread walks the tile's valid rows
 // (64, or fewer in the segment's last tile) and divides by their count.
 __global__ __launch_bounds__(128) void pool_q_kernel(const uint16_t* __restrict__ q, int H,
-                                                     int64_t S_t, int n_v, int64_t V_v,
+                                                     int ldh, int64_t S_t, int n_v, int64_t V_v,
                                                      double* __restrict__ qbar64) {
     const int u = blockIdx.x;
     const int h = blockIdx.y * 8 + (threadIdx.x >> 4);
@@ -33,7 +33,7 @@ __global__ __launch_bounds__(128) void pool_q_kernel(const uint16_t* __restrict_
     if (h >= H) return;
     const int64_t rem = V_v - (int64_t)u * kT;
     const int n = rem >= kT ? kT : (int)rem;
-    const int64_t rs = (int64_t)H * kD;
+    const int64_t rs = (int64_t)ldh * kD;
     const uint16_t* p = q + (S_t + (int64_t)u * kT) * rs + (int64_t)h * kD + c * 8;
     double acc[8];
 #pragma unroll
@@ -111,7 +111,7 @@ __device__ __forceinline__ float bf16_round_f(float x) {
 // row of the tile: RMSNorm (+ RoPE for video tokens) of Q into q_out, and for
 // video tiles the FP32 mean of the preprocessed rows over the valid ones.
 __global__ __launch_bounds__(128) void prep_q_kernel(const uint16_t* __restrict__ q,
-                                                     PrepArgs pa, int H, int n_t, int n_v,
+                                                     PrepArgs pa, int H, int ldh, int n_t, int n_v,
                                                      int64_t S_t, int64_t V_t, int64_t V_v,
                                                      int64_t V_a, int64_t S_v,
                                                      uint16_t* __restrict__ q_out,
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(128) void prep_q_kernel(const uint16_t* __restrict_
     const int c = threadIdx.x & 15;
     const bool active = h < H;
     const int hh = active ? h : H - 1;
-    const int64_t rs = (int64_t)H * kD;
+    const int64_t rs = (int64_t)ldh * kD;
     const bool video = j >= n_t && j < n_t + n_v;
     // first token row of the tile and its valid rows
     int64_t row0, valid;
@@ -204,7 +204,7 @@ constexpr int kPitch = kD + 8;  // LDS row pitch in bf16 elements (272 bytes)
 
 __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ v, int H,
-                                                      int n_t, int n_v, int N, int64_t S_t,
+                                                      int ldh, int n_t, int n_v, int N, int64_t S_t,
                                                       int64_t S_v, int64_t V_t, int64_t V_v,
                                                       int64_t V_a, PrepArgs pa,
                                                       float* __restrict__ kbar_t,
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t* __restrict
     const int t = blockIdx.x;
     const int h = blockIdx.y;
     const int tid = threadIdx.x;
-    const int64_t rs = (int64_t)H * kD;
+    const int64_t rs = (int64_t)ldh * kD;
     const int64_t src = (int64_t)t * kT * rs + (int64_t)h * kD;
     // valid rows of this tile; padding rows are stored as zeros
     int64_t valid;
@@ -321,17 +321,17 @@ hipError_t launch_pool_pack(const uint16_t* q, const uint16_t* k, const uint16_t
         ka = qa;
         ka.gamma = prep->gamma_k;
         hipLaunchKernelGGL(prep_q_kernel, dim3(s.N, (s.H + 7) / 8), dim3(128), 0, stream, q, qa, s.H,
-                           s.n_t, s.n_v, s.S_t, s.V_t, s.V_v, s.V_a, s.S_v, q_out,
+                           s.ldh, s.n_t, s.n_v, s.S_t, s.V_t, s.V_v, s.V_a, s.S_v, q_out,
                            (double*)(ws + L.qbar64));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     } else if (s.n_v > 0) {
         hipLaunchKernelGGL(pool_q_kernel, dim3(s.n_v, (s.H + 7) / 8), dim3(128), 0, stream, q, s.H,
-                           s.S_t, s.n_v, s.V_v, (double*)(ws + L.qbar64));
+                           s.ldh, s.S_t, s.n_v, s.V_v, (double*)(ws + L.qbar64));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(pack_kv_kernel, dim3(s.N, s.H), dim3(256), 0, stream, k, v, s.H, s.n_t, s.n_v,
+    hipLaunchKernelGGL(pack_kv_kernel, dim3(s.N, s.H), dim3(256), 0, stream, k, v, s.H, s.ldh, s.n_t, s.n_v,
                        s.N, s.S_t, s.S_v, s.V_t, s.V_v, s.V_a, ka, (float*)(ws + L.kbar_t),
                        (float*)(ws + L.vbar), (uint16_t*)(ws + L.kpack), (uint16_t*)(ws + L.vpack));
     return hipGetLastError();

@@ -49,14 +49,14 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // of K in float64 and writes the float32 means into the packed layout.
 __global__ __launch_bounds__(128) void subpool_kernel(const uint16_t* __restrict__ q,
                                                       const uint16_t* __restrict__ k, int H,
-                                                      int64_t S_t, int n_v, int n_c,
+                                                      int ldh, int64_t S_t, int n_v, int n_c,
                                                       float* __restrict__ qsub,
                                                       float* __restrict__ ksub) {
     const int u = blockIdx.x;
     const int h = blockIdx.y * 8 + (threadIdx.x >> 4);
     const int cc = threadIdx.x & 15;  // dims 8 cc .. 8 cc + 7
     if (h >= H) return;
-    const int64_t rs = (int64_t)H * kD;
+    const int64_t rs = (int64_t)ldh * kD;
     const int grp = u >> 2;
     const int g = cc >> 2, i0 = 2 * (cc & 3);
     const int64_t gbase = ((int64_t)h * n_c + grp) * 8;  // in units of [64][4] floats
@@ -270,7 +270,7 @@ hipError_t launch_subblock_route(const uint16_t* q, const uint16_t* k, const Sha
     if (s.n_v == 0) return hipSuccess;
     const int n_c = (s.n_v + 3) / 4;
     hipLaunchKernelGGL(subpool_kernel, dim3(4 * n_c, (s.H + 7) / 8), dim3(128), 0, stream, q, k,
-                       s.H, s.S_t, s.n_v, n_c, (float*)(ws + L.qsub), (float*)(ws + L.ksub));
+                       s.H, s.ldh, s.S_t, s.n_v, n_c, (float*)(ws + L.qsub), (float*)(ws + L.ksub));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // rows of 4 RT query tiles x ldw float64 scores must fit the 160 KiB of LDS

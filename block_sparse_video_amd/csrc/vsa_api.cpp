@@ -28,6 +28,7 @@ vsa_status make_shape(int32_t H, int64_t S_t, int64_t S_v, int64_t S_a, Shape* s
     if (S > VSA_MAX_TOKENS) return VSA_ERR_TOO_LARGE;
     if (S_v / VSA_TILE > VSA_MAX_VIDEO_TILES) return VSA_ERR_TOO_LARGE;
     s->H = H;
+    s->ldh = H;
     s->S_t = S_t;
     s->S_v = S_v;
     s->S_a = S_a;
@@ -258,6 +259,62 @@ vsa_status vsa_forward(const void* q, const void* k, const void* v, const void* 
     if (e == hipSuccess)
         e = vsa::launch_fine_attention((const uint16_t*)q, (const uint16_t*)gate,
                                        selected_tiles, (uint16_t*)out, s, ws, L, strm);
+    return from_hip(e);
+}
+
+vsa_status vsa_forward_noalloc(const void* q, const void* k, const void* v, const void* gate,
+                               int32_t num_heads, int64_t text_len, int64_t video_len,
+                               int64_t audio_len, float topk_frac, void* out,
+                               int32_t* selected_tiles, void* stream) {
+    if (!q || !k || !v || !out) return VSA_ERR_NULL_POINTER;
+    if (video_len != 0 && (!gate || !selected_tiles)) return VSA_ERR_NULL_POINTER;
+    Shape s;
+    vsa_status st = make_shape(num_heads, text_len, video_len, audio_len, &s);
+    if (st != VSA_OK) return st;
+    if ((st = check_topk(topk_frac, &s)) != VSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        (gate && !aligned(gate, 16)) || (selected_tiles && !aligned(selected_tiles, 16)))
+        return VSA_ERR_MISALIGNED;
+    // the largest group of heads whose workspace fits the array (the layout
+    // grows with the head count)
+    const size_t cap = VSA_NOALLOC_SCRATCH_BYTES;
+    Shape g = s;
+    g.H = 1;
+    if (vsa::make_layout(g).total > cap) return VSA_ERR_TOO_LARGE;
+    int32_t lo = 1, hi = s.H;
+    while (lo < hi) {
+        const int32_t mid = lo + (hi - lo + 1) / 2;
+        g.H = mid;
+        if (vsa::make_layout(g).total <= cap) lo = mid;
+        else hi = mid - 1;
+    }
+    const int32_t per_group = lo;
+    if ((st = check_device()) != VSA_OK) return st;
+    void* scratch = nullptr;
+    size_t scratch_bytes = 0;
+    if (vsa::noalloc_scratch(&scratch, &scratch_bytes) != hipSuccess) return VSA_ERR_HIP;
+    if (scratch_bytes < cap) return VSA_ERR_HIP;
+    hipStream_t strm = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)scratch;
+    hipError_t e = hipSuccess;
+    for (int32_t h0 = 0; h0 < s.H && e == hipSuccess; h0 += per_group) {
+        // heads h0 .. h0 + c.H - 1, reading and writing the caller's tensors in
+        // place: row stride stays the caller's head count
+        Shape c = s;
+        c.H = s.H - h0 < per_group ? s.H - h0 : per_group;
+        c.ldh = s.H;
+        const Layout L = vsa::make_layout(c);
+        const int64_t hoff = (int64_t)h0 * VSA_HEAD_DIM;
+        const uint16_t* qh = (const uint16_t*)q + hoff;
+        const uint16_t* kh = (const uint16_t*)k + hoff;
+        const uint16_t* vh = (const uint16_t*)v + hoff;
+        const uint16_t* gh = gate ? (const uint16_t*)gate + hoff : nullptr;
+        uint16_t* oh = (uint16_t*)out + hoff;
+        int32_t* selh = selected_tiles ? selected_tiles + (int64_t)h0 * s.n_v * s.k : nullptr;
+        e = vsa::launch_pool_pack(qh, kh, vh, c, ws, L, strm);
+        if (e == hipSuccess && c.n_v > 0) e = vsa::launch_select_coarse(c, selh, ws, L, strm);
+        if (e == hipSuccess) e = vsa::launch_fine_attention(qh, gh, selh, oh, c, ws, L, strm);
+    }
     return from_hip(e);
 }
 

@@ -15,7 +15,10 @@ constexpr int kT = 64;    // tokens per tile
 constexpr size_t kAlign = 256;
 
 struct Shape {
-    int32_t H;
+    int32_t H;                 // heads this call computes
+    // heads per token row of the caller's q/k/v/gate/out (the row stride is
+    // ldh * 128 elements): H, unless a call works on a slice of the heads
+    int32_t ldh;
     int64_t S_t, S_v, S_a, S;
     int32_t n_t, n_v, n_a, N;  // tile counts
     int32_t k;                 // selected tiles per video query tile
@@ -129,6 +132,10 @@ hipError_t launch_fine_attention(const uint16_t* q, const uint16_t* gate,
 // SubBlock router: sub-block means of Q and K, scores and top-k (s.k tiles).
 hipError_t launch_subblock_route(const uint16_t* q, const uint16_t* k, const Shape& s,
                                  int32_t* sel, uint8_t* ws, const Layout& L, hipStream_t stream);
+
+// Device address and size of the fixed scratch array of vsa_forward_noalloc
+// on the current device (looked up once per device, then cached).
+hipError_t noalloc_scratch(void** out, size_t* bytes);
 
 hipError_t launch_project_qkvg(const uint16_t* x, const uint16_t* w, uint16_t* const out[4],
                                int64_t tokens, int hidden, int n_out, hipStream_t stream);

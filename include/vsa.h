@@ -265,6 +265,31 @@ vsa_status vsa_project_qkvg(const void* x, const void* w, int64_t tokens, int32_
                             int32_t num_heads, void* q, void* k, void* v, void* gate,
                             void* stream);
 
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * vsa_forward with the workspace taken from a fixed array inside the library
+ * instead of from the caller or from hipMalloc: VSA_NOALLOC_SCRATCH_BYTES of
+ * device memory per device, set up on the first call on that device (which
+ * looks up its address with hipGetSymbolAddress) and held until the process
+ * ends.  The call allocates nothing and issues no memset; the caller still
+ * passes q, k, v, gate, out and selected_tiles as for vsa_forward, with the
+ * same meaning, layout and checks.
+ * Heads are processed in consecutive groups small enough for one group's
+ * workspace to fit the array (results are bit-identical to vsa_forward's).
+ * A shape whose single head needs more workspace than the array holds is
+ * rejected with VSA_ERR_TOO_LARGE, before any HIP call (at the 10 s shape of
+ * 1,166 tiles one head needs about 45 MB, so about 5 heads run per group).
+ * Every call on a device shares that device's array, and the array keeps the
+ * last call's contents (nothing in it needs to start at zero: work-queue
+ * counters are cleared by a kernel at each launch).  Calls that overlap in
+ * time on one device -- other streams or other host threads -- race on the
+ * array and give wrong results: serialise them. */
+#define VSA_NOALLOC_SCRATCH_BYTES (256u << 20)
+vsa_status vsa_forward_noalloc(const void* q, const void* k, const void* v, const void* gate,
+                               int32_t num_heads, int64_t text_len, int64_t video_len,
+                               int64_t audio_len, float topk_frac, void* out,
+                               int32_t* selected_tiles, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -238,3 +238,34 @@ def test_padded_validation(kw, code):
 
 def test_padded_without_video_allows_null_gate_and_selection():
     assert padded(vid=0, vv=0, g=None, sel=None, wsb=10) == WORKSPACE
+
+
+def noalloc(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, h=2, t=64, vid=640, au=64, frac=0.2, out=FAKE,
+             sel=FAKE)
+    a.update(kw)
+    return _native.load().vsa_forward_noalloc(a["q"], a["k"], a["v"], a["g"], a["h"], a["t"],
+                                              a["vid"], a["au"], a["frac"], a["out"], a["sel"],
+                                              None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULLP), (dict(out=None), NULLP), (dict(g=None), NULLP), (dict(sel=None), NULLP),
+    (dict(h=0), SHAPE), (dict(vid=100), UNALIGNED), (dict(frac=0.0), TOPK),
+    (dict(q=FAKE + 2), MISALIGNED), (dict(sel=FAKE + 4), MISALIGNED),
+    (dict(h=2048), TOO_LARGE),
+    # one head of 16,384 video tiles needs ~0.6 GB of workspace: beyond the array
+    (dict(h=1, vid=64 * 16384), TOO_LARGE),
+])
+def test_noalloc_validation(kw, code):
+    assert noalloc(**kw) == code
+
+
+def test_noalloc_limit_is_one_head_of_workspace():
+    cap = 256 << 20
+    # the largest video length whose one-head workspace fits is accepted past
+    # the size check (it then fails only at the device check on this host)
+    n_ok = max(n for n in range(1, 16385, 7)
+               if bsv.vsa_workspace_bytes(1, 64, 64 * n, 64) <= cap)
+    assert noalloc(h=1, vid=64 * n_ok) not in (TOO_LARGE, SHAPE, UNALIGNED)
+    assert noalloc(h=1, vid=64 * (n_ok + 7)) == TOO_LARGE
