@@ -29,7 +29,11 @@
 //   O^T[qb] (128 dims x 32 queries) += V^T P^T  -- eight more MFMAs
 // Software pipeline: step x issues the S^T MFMAs of half-tile x+1 and the PV
 // MFMAs of half-tile x-1 while the vector unit computes the numerators of
-// half-tile x, so no MFMA of a step depends on that step's vector work.
+// half-tile x, so no MFMA of a step depends on that step's vector work.  The
+// instruction order inside a step is fixed by hand: each MFMA is followed by
+// its share of the vector work (one element pair of the numerators) and each
+// MFMA pair by one 1 KiB operand copy, so the vector unit works while the
+// matrix unit is busy.
 //
 // Accumulator layout of a 32x32 MFMA (lane l, element i of the 16 floats):
 //   row = 8*(i/4) + 4*(l/32) + (i%4), column = l%32.
@@ -272,31 +276,12 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
     asm volatile("" ::: "memory");
 }
 
-// Wait for every outstanding LDS read (and scalar load) of this wave.
+// Wait for every outstanding LDS read (and scalar load) of this wave.  Issued
+// through the builtin, so the compiler knows that everything it tracks on
+// this counter is complete afterwards and inserts no further waits for it.
 __device__ __forceinline__ void wait_lgkm() {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-}
-
-// Reference-scaled softmax numerators of one 32-query block over one
-// half-tile: P = 2^(s * scale_log2 - m_ref) with a per-column reference
-// m_ref that stays fixed for the whole key list (see the kernel), so O never
-// needs rescaling inside the loop.  Returns P as two bf16 operands (keys
-// 0..15 and 16..31 of the half-tile, in operand order) and adds this lane's
-// share of the denominator to l_run.
-__device__ __forceinline__ void numerators(const f32x16& s, float c2, float m_ref, float& l_run,
-                                           bf16x8& p0, bf16x8& p1) {
-    f32x8 a, b;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        a[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], c2, -m_ref));
-        b[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 + e], c2, -m_ref));
-    }
-    float lsum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lsum += a[e] + b[e];
-    l_run += lsum;
-    p0 = __builtin_convertvector(a, bf16x8);
-    p1 = __builtin_convertvector(b, bf16x8);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
 }
 
 // Column max of one S^T block (16 values here, 16 in lane ^ 32), times scale_log2.
@@ -379,6 +364,28 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
             }
             return a.n_v + it - a.kk;
         };
+        // request the raw selection word for list position `it` (clamped to
+        // the list) with an ordinary scalar load from a uniform address in the
+        // constant address space; decode it later (tile_dec), so the load's own
+        // wait is paid where nothing else is pending.  Positions that need no
+        // word load a harmless one (the work-queue counters).
+        auto tile_req = [&](int it) -> int {
+            if (it >= n_tiles) it = n_tiles - 1;
+            const bool need = video && it >= a.n_t && it < a.n_t + a.kk;
+            const int32_t* src = need ? selrow + (it - a.n_t) : (const int32_t*)a.sched;
+            const uint64_t pa = (uint64_t)(uintptr_t)src;
+            const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)pa);
+            const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(pa >> 32));
+            typedef __attribute__((address_space(4))) const int32_t* const_i32_ptr;
+            return *(const_i32_ptr)(((uint64_t)hi << 32) | lo);
+        };
+        auto tile_dec = [&](int it, int word) -> int {
+            if (it >= n_tiles) it = n_tiles - 1;
+            if (!video) return it0 + it;
+            if (it < a.n_t) return it;
+            if (it < a.n_t + a.kk) return a.n_t + (word < 0 ? 0 : (word >= a.n_v ? a.n_v - 1 : word));
+            return a.n_v + it - a.kk;
+        };
         // per-head bases of the packed operands (bytes): 16 KiB per tile and
         // tensor, two 8 KiB half-tiles each
         const char* kbase = (const char*)(a.kpack + (int64_t)h * a.N * (kT * kD));
@@ -455,7 +462,8 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
             // (x >> 1), staged in K slot x mod 3 and V slot x mod 2.  Step x
             // computes
             //   S^T(x+1) = K(x+1) Q^T              (16 MFMAs)
-            //   P(x)     = numerators of S^T(x)     (vector ALU)
+            //   P(x)     = 2^(S^T(x) scale_log2 - m_ref), rounded to bf16, and
+            //              its sum added to the denominators (vector ALU)
             //   O       += V(x-1) P(x-1)            (16 MFMAs)
             // so none of its matrix work waits for its own vector work.  Operands
             // enter registers one step ahead (K(x+2) in the middle of step x,
@@ -510,18 +518,17 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
             int cur = t0, nxt = t1;
             int xm3 = 0;
             for (int t = 0; t < n_tiles; ++t) {
-                const int nn = tile_at(t + 2);
+                int nn = 0, nn_word = 0;
                 const int rows_cur = tile_rows(a, cur);  // token rows of the tile in use
 #pragma unroll
                 for (int pp = 0; pp < 2; ++pp) {
                     // step x = 2t + pp
                     const int k_wr = xm3 == 2 ? 0 : xm3 + 1;  // (x + 4) mod 3
                     const int k_rd = xm3 == 0 ? 2 : xm3 - 1;  // (x + 2) mod 3
-                    wait_lgkm();  // kop = K(x+1), vop = V(x-1)
                     // V(x+1): (t, half 1) or (t+1, half 0); K(x+4): (t+2, half pp),
                     // issued one 1 KiB piece at a time between MFMAs below
                     const char* vsrc = vbase + (pp == 0 ? cur : nxt) * kTileBytes + (pp ^ 1) * kHalfBytes;
-                    const char* ksrc = kbase + nn * kTileBytes + pp * kHalfBytes;
+                    const char* ksrc = kbase + pp * kHalfBytes;  // + nn * kTileBytes below
                     const uint32_t vdst = vslot[pp ^ 1], kdst = kslot(k_wr);
                     f32x16 n0 = zero16, n1 = zero16;
                     bf16x8 pc[2][2];
@@ -533,26 +540,83 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
                             mask_keys(sc[1], nvh, g);
                         }
                     }
+                    // The step in issue order.  Every MFMA is followed by one element
+                    // pair (e, 8 + e) of the numerators of S^T(x) (first half: block 0
+                    // with the S^T MFMAs; second half: block 1 with the PV MFMAs) and
+                    // every MFMA pair by one operand copy.  MFMAs and numerators have no
+                    // side effects, so instruction selection would otherwise gather
+                    // them next to their uses (16 MFMAs in a row, the exponentials of
+                    // two steps in a row): each result passes through an empty asm
+                    // statement right where it is made, which fixes its place in the
+                    // program order, and sched_barrier(0) keeps the machine scheduler
+                    // from merging the groups.  The denominators add the pairs in the
+                    // order e = 0..7, as a plain loop would.
+                    f32x8 na0, nb0, na1, nb1;
+                    float ls0 = 0.0f, ls1 = 0.0f;
+                    const float mr0 = m_ref[0], mr1 = m_ref[1];
 #pragma unroll
                     for (int s8 = 0; s8 < 8; ++s8) {
                         n0 = mfma32(kop[s8], qf[0][s8], n0);
+                        asm volatile("" : "+a"(n0));
+                        __builtin_amdgcn_sched_barrier(0);
+                        na0[s8] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][s8], c2, -mr0));
+                        nb0[s8] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][8 + s8], c2, -mr0));
+                        __builtin_amdgcn_sched_barrier(0);
                         n1 = mfma32(kop[s8], qf[1][s8], n1);
+                        asm volatile("" : "+a"(n1));
+                        __builtin_amdgcn_sched_barrier(0);
+                        // exp2 results are >= +0, so starting from the first pair's sum
+                        // equals adding it to 0
+                        ls0 = s8 == 0 ? na0[s8] + nb0[s8] : ls0 + (na0[s8] + nb0[s8]);
+                        asm volatile("" ::"v"(na0[s8]), "v"(nb0[s8]), "v"(ls0));
+                        if (s8 == 0) {
+                            // the V slot written next was read at the end of the last
+                            // step: those reads must be complete first.  Waiting here,
+                            // one MFMA pair into the step, lets their latency pass
+                            // under matrix work.  In the first step of a tile the next
+                            // tile index is requested right after the wait and used at
+                            // the end of this half, so no scalar load is ever pending
+                            // where the compiler waits for LDS reads.
+                            wait_lgkm();
+                            if (pp == 0) nn_word = tile_req(t + 2);
+                        }
                         fetch_piece(vdst + 1024u * s8, vsrc, voff[s8]);
-                        __builtin_amdgcn_sched_barrier(0x406);
+                        __builtin_amdgcn_sched_barrier(0);
                     }
-                    numerators(sc[0], c2, m_ref[0], l_run[0], pc[0][0], pc[0][1]);
+                    l_run[0] += ls0;
+                    pc[0][0] = __builtin_convertvector(na0, bf16x8);
+                    pc[0][1] = __builtin_convertvector(nb0, bf16x8);
+                    asm volatile("" ::"v"(pc[0][0]), "v"(pc[0][1]));
+                    if (pp == 0) {
+                        asm volatile("" : "+s"(nn_word));
+                        nn = tile_dec(t + 2, nn_word);
+                    }
                     wait_vmcnt(24);  // K(x+2)
                     read_ops(kop, kslot(k_rd), lane);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int db = 0; db < 4; ++db)
 #pragma unroll
                         for (int m = 0; m < 2; ++m) {
-                            o[0][db] = mfma32(vop[2 * db + m], pprev[0][m], o[0][db]);
-                            o[1][db] = mfma32(vop[2 * db + m], pprev[1][m], o[1][db]);
-                            fetch_piece(kdst + 1024u * (2 * db + m), ksrc, voff[2 * db + m]);
-                            __builtin_amdgcn_sched_barrier(0x406);
+                            const int e = 2 * db + m;
+                            o[0][db] = mfma32(vop[e], pprev[0][m], o[0][db]);
+                            asm volatile("" : "+a"(o[0][db]));
+                            __builtin_amdgcn_sched_barrier(0);
+                            na1[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[1][e], c2, -mr1));
+                            nb1[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[1][8 + e], c2, -mr1));
+                            __builtin_amdgcn_sched_barrier(0);
+                            o[1][db] = mfma32(vop[e], pprev[1][m], o[1][db]);
+                            asm volatile("" : "+a"(o[1][db]));
+                            __builtin_amdgcn_sched_barrier(0);
+                            ls1 = e == 0 ? na1[e] + nb1[e] : ls1 + (na1[e] + nb1[e]);
+                            asm volatile("" ::"v"(na1[e]), "v"(nb1[e]), "v"(ls1));
+                            fetch_piece(kdst + 1024u * e, ksrc + nn * kTileBytes, voff[e]);
+                            __builtin_amdgcn_sched_barrier(0);
                         }
-                    numerators(sc[1], c2, m_ref[1], l_run[1], pc[1][0], pc[1][1]);
+                    l_run[1] += ls1;
+                    pc[1][0] = __builtin_convertvector(na1, bf16x8);
+                    pc[1][1] = __builtin_convertvector(nb1, bf16x8);
+                    asm volatile("" ::"v"(pc[1][0]), "v"(pc[1][1]));
                     wait_vmcnt(24);  // V(x)
                     read_ops(vop, vslot[pp], lane);
                     sc[0] = n0;
