@@ -79,6 +79,16 @@ def _load():
         lib.vsa_oracle_subblock_select_rows.argtypes = [_P, _P, _I32, _I64, _I64, _I64, _F64, _P,
                                                         _I64, _P, _P, _P, _P, _P, ctypes.c_int]
         lib.vsa_oracle_subblock_select_rows.restype = _I32
+        lib.vsa_oracle_subblock_select_whole.argtypes = [_P, _P, _I32, _I64, _I64, _I64, _F64,
+                                                         _P, _P, _P, _P, _P, ctypes.c_int]
+        lib.vsa_oracle_subblock_select_whole.restype = _I32
+        lib.vsa_oracle_subblock_select_whole_rows.argtypes = [_P, _P, _I32, _I64, _I64, _I64,
+                                                              _F64, _P, _I64, _P, _P, _P, _P, _P,
+                                                              ctypes.c_int]
+        lib.vsa_oracle_subblock_select_whole_rows.restype = _I32
+        lib.vsa_oracle_fine_lists.argtypes = [_P, _P, _P, _I32, _I64, _P, _I32, _P, _I64, _P, _P,
+                                              ctypes.c_int]
+        lib.vsa_oracle_fine_lists.restype = _I32
         lib.vsa_oracle_bf16_from_f64.argtypes = [_F64]
         lib.vsa_oracle_bf16_from_f64.restype = ctypes.c_uint16
         lib.vsa_oracle_default_threads.argtypes = []
@@ -383,3 +393,76 @@ def subblock_select_rows(q, k, text_len, video_len, audio_len, sparsity, rows, t
     if r < 0:
         raise ValueError("bad arguments")
     return {"k": kk, "qsub": qsub, "ksub": ksub, "sel": sel, "kth": kth, "scores": scores}
+
+
+def subblock_select_whole(q, k, text_len, video_len, audio_len, sparsity, want_scores=False,
+                          threads=None) -> dict:
+    """The SubBlock router over the whole sequence: every one of the N tiles
+    is a query tile and a candidate key tile.  Returns qsub, ksub [H][N][4][128],
+    sel [H][N][k] (global tile indices, ascending), kth [H][N] and, when asked,
+    scores [H][N][N]; k = subblock_count(N, sparsity)."""
+    s = text_len + video_len + audio_len
+    h = q.shape[1]
+    q, k = (_check_tensor(x, s, h) for x in (q, k))
+    n = s // TILE
+    kk = subblock_count(n, sparsity)
+    if kk < 0 or s % TILE or text_len % TILE or video_len % TILE:
+        raise ValueError("bad arguments")
+    qsub = np.empty((h, n, 4, HEAD_DIM), np.float32)
+    ksub = np.empty_like(qsub)
+    sel = np.empty((h, n, kk), np.int32)
+    kth = np.empty((h, n), np.float64)
+    scores = np.empty((h, n, n), np.float64) if want_scores else None
+    r = _load().vsa_oracle_subblock_select_whole(_ptr(q), _ptr(k), h, text_len, video_len,
+                                                 audio_len, frac_as_passed(sparsity), _ptr(qsub),
+                                                 _ptr(ksub), _ptr(sel), _ptr(kth), _ptr(scores),
+                                                 threads or 0)
+    if r < 0:
+        raise ValueError("bad arguments")
+    return {"k": kk, "qsub": qsub, "ksub": ksub, "sel": sel, "kth": kth, "scores": scores}
+
+
+def subblock_select_whole_rows(q, k, text_len, video_len, audio_len, sparsity, rows,
+                               threads=None) -> dict:
+    """subblock_select_whole for the (head, tile) rows listed as pairs."""
+    s = text_len + video_len + audio_len
+    h = q.shape[1]
+    q, k = (_check_tensor(x, s, h) for x in (q, k))
+    n = s // TILE
+    kk = subblock_count(n, sparsity)
+    if kk < 0 or s % TILE:
+        raise ValueError("bad arguments")
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+    flat = np.ascontiguousarray(rows[:, 0] * n + rows[:, 1])
+    m = len(flat)
+    qsub = np.empty((h, n, 4, HEAD_DIM), np.float32)
+    ksub = np.empty_like(qsub)
+    sel = np.empty((m, kk), np.int32)
+    kth = np.empty(m, np.float64)
+    scores = np.empty((m, n), np.float64)
+    r = _load().vsa_oracle_subblock_select_whole_rows(
+        _ptr(q), _ptr(k), h, text_len, video_len, audio_len, frac_as_passed(sparsity), _ptr(flat),
+        m, _ptr(qsub), _ptr(ksub), _ptr(sel), _ptr(kth), _ptr(scores), threads or 0)
+    if r < 0:
+        raise ValueError("bad arguments")
+    return {"k": kk, "qsub": qsub, "ksub": ksub, "sel": sel, "kth": kth, "scores": scores}
+
+
+def fine_lists(q, k, v, lists, rows, threads=None):
+    """Rows `rows` of every head, each query tile j attending to the keys of
+    its own key tiles lists[h][j] ([H][N][k], global indices); no coarse term,
+    no gate.  Returns (bfloat16 bits [n_rows][H][128], float64 [n_rows][H][128])."""
+    s, h = q.shape[0], q.shape[1]
+    q, k, v = (_check_tensor(x, s, h) for x in (q, k, v))
+    lists = np.ascontiguousarray(lists, dtype=np.int32)
+    if lists.ndim != 3 or lists.shape[:2] != (h, s // TILE):
+        raise ValueError("lists must be [H][N][k]")
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out_b = np.empty((len(rows), h, HEAD_DIM), np.uint16)
+    out_d = np.empty((len(rows), h, HEAD_DIM), np.float64)
+    r = _load().vsa_oracle_fine_lists(_ptr(q), _ptr(k), _ptr(v), h, s, _ptr(lists),
+                                      lists.shape[2], _ptr(rows), len(rows), _ptr(out_b),
+                                      _ptr(out_d), threads or 0)
+    if r < 0:
+        raise ValueError("bad arguments")
+    return out_b, out_d

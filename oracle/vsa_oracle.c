@@ -639,3 +639,139 @@ int32_t vsa_oracle_subblock_select_rows(const uint16_t* q, const uint16_t* k, in
     run_pool(subscore_item, &c, n_rows, scratch, threads);
     return kk;
 }
+
+/* ------------------------------------------------------------------------ */
+/* SubBlock router, whole-sequence mode (the page's own reading)             */
+/* ------------------------------------------------------------------------ */
+
+/* Every 64-token tile of the joint [text | video | audio] sequence is both a
+ * query tile and a candidate key tile: N = S / 64 tiles, tile j holding
+ * tokens 64j .. 64j + 63.  Piece means, scores and the ranking are exactly
+ * those of the video mode above, taken over all N tiles instead of the n_v
+ * video tiles: the ranking of each (head, query tile) row runs over every
+ * key tile of the sequence, and the kept count is
+ * vsa_oracle_subblock_count(N, sparsity).  Selected indices are global tile
+ * indices 0..N-1, ascending.  Outputs as vsa_oracle_subblock_select with n_v
+ * replaced by N. */
+int32_t vsa_oracle_subblock_select_whole(const uint16_t* q, const uint16_t* k, int32_t H,
+                                         int64_t S_t, int64_t S_v, int64_t S_a, double sparsity,
+                                         float* qsub, float* ksub, int32_t* sel, double* kth,
+                                         double* scores, int threads) {
+    if (H < 1 || S_t % T || S_v % T || S_a % T || S_t < 0 || S_v < 0 || S_a < 0) return -1;
+    const int64_t N = (S_t + S_v + S_a) / T;
+    const int32_t kk = vsa_oracle_subblock_count(N, sparsity);
+    if (kk < 0) return -1;
+    if (N == 0) return 0;
+    /* the video mode's machinery over rows 0 .. S - 1: tile j starts at row 64j */
+    sub_ctx_t c = {q, k, H, 0, N, kk, qsub, ksub, sel, kth, scores, NULL};
+    run_pool(subpool_item, &c, (int64_t)H * N, 0, threads);
+    size_t scratch = sizeof(double) * (size_t)N + sizeof(scored_t) * (size_t)N;
+    run_pool(subscore_item, &c, (int64_t)H * N, scratch, threads);
+    return kk;
+}
+
+/* As vsa_oracle_subblock_select_whole for the listed rows only (rows[i] =
+ * h * N + j): piece means of every tile, then sel [n_rows][k], kth [n_rows],
+ * scores [n_rows][N] (may be NULL). */
+int32_t vsa_oracle_subblock_select_whole_rows(const uint16_t* q, const uint16_t* k, int32_t H,
+                                              int64_t S_t, int64_t S_v, int64_t S_a,
+                                              double sparsity, const int64_t* rows,
+                                              int64_t n_rows, float* qsub, float* ksub,
+                                              int32_t* sel, double* kth, double* scores,
+                                              int threads) {
+    if (H < 1 || S_t % T || S_v % T || S_a % T || S_t < 0 || S_v < 0 || S_a < 0 || n_rows < 0)
+        return -1;
+    const int64_t N = (S_t + S_v + S_a) / T;
+    const int32_t kk = vsa_oracle_subblock_count(N, sparsity);
+    if (kk < 0) return -1;
+    for (int64_t i = 0; i < n_rows; ++i)
+        if (rows[i] < 0 || rows[i] >= (int64_t)H * N) return -1;
+    if (N == 0) return 0;
+    sub_ctx_t c = {q, k, H, 0, N, kk, qsub, ksub, sel, kth, scores, rows};
+    run_pool(subpool_item, &c, (int64_t)H * N, 0, threads);
+    size_t scratch = sizeof(double) * (size_t)N + sizeof(scored_t) * (size_t)N;
+    run_pool(subscore_item, &c, n_rows, scratch, threads);
+    return kk;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Fine attention over per-tile key lists                                     */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const uint16_t *q, *k, *v;
+    int32_t H;
+    int64_t S;
+    const int32_t* lists; /* [H][N][kk] global key-tile indices */
+    int32_t kk;
+    const int64_t* rows;
+    uint16_t* out_bf16; /* [n_rows][H][128] */
+    double* out_f64;    /* [n_rows][H][128] or NULL */
+} lists_ctx_t;
+
+/* Query row i (tile j = i / 64) of head h attends to the keys of the tiles
+ * lists[h][j][0 .. kk): one softmax over those keys with logits
+ * q.k / sqrt(128), no coarse term and no gate; the result is rounded once to
+ * bfloat16.  This is the fine step of the whole-sequence router (section
+ * "How SubBlock Sparse Attention Works": the kept key blocks of each query
+ * block go to the block-sparse attention kernel). */
+static void lists_item(void* p, int64_t item, void* scratch) {
+    lists_ctx_t* c = (lists_ctx_t*)p;
+    const int32_t H = c->H;
+    const int64_t ri = item / H;
+    const int32_t h = (int32_t)(item % H);
+    const int64_t i = c->rows[ri];
+    const int64_t N = c->S / T;
+    const double alpha = 1.0 / sqrt((double)D);
+    double* logit = (double*)scratch;
+    const int32_t* lst = c->lists + ((int64_t)h * N + i / T) * c->kk;
+    double qi[D];
+    for (int d = 0; d < D; ++d) qi[d] = bf16_to_f64(c->q[(i * H + h) * D + d]);
+    double m = -INFINITY;
+    int64_t nk = 0;
+    for (int32_t t = 0; t < c->kk; ++t)
+        for (int r = 0; r < T; ++r) {
+            const int64_t j = (int64_t)lst[t] * T + r;
+            const uint16_t* kj = c->k + (j * H + h) * D;
+            double s = 0.0;
+            for (int d = 0; d < D; ++d) s += qi[d] * bf16_to_f64(kj[d]);
+            logit[nk] = alpha * s;
+            if (logit[nk] > m) m = logit[nk];
+            ++nk;
+        }
+    double den = 0.0, o[D];
+    for (int d = 0; d < D; ++d) o[d] = 0.0;
+    nk = 0;
+    for (int32_t t = 0; t < c->kk; ++t)
+        for (int r = 0; r < T; ++r) {
+            const int64_t j = (int64_t)lst[t] * T + r;
+            const double e = exp(logit[nk++] - m);
+            den += e;
+            const uint16_t* vj = c->v + (j * H + h) * D;
+            for (int d = 0; d < D; ++d) o[d] += e * bf16_to_f64(vj[d]);
+        }
+    const int64_t base = (ri * H + h) * D;
+    for (int d = 0; d < D; ++d) {
+        const double y = o[d] / den;
+        if (c->out_f64) c->out_f64[base + d] = y;
+        c->out_bf16[base + d] = vsa_oracle_bf16_from_f64(y);
+    }
+}
+
+/* Output rows `rows` of every head, each query tile attending to its own list
+ * of kk key tiles (lists [H][N][kk], global indices in [0, N), distinct).
+ * Returns 0, or -1 on bad arguments. */
+int32_t vsa_oracle_fine_lists(const uint16_t* q, const uint16_t* k, const uint16_t* v, int32_t H,
+                              int64_t S, const int32_t* lists, int32_t kk, const int64_t* rows,
+                              int64_t n_rows, uint16_t* out_bf16, double* out_f64, int threads) {
+    if (H < 1 || S <= 0 || S % T || kk < 1 || n_rows < 0) return -1;
+    const int64_t N = S / T;
+    if (kk > N) return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        if (rows[r] < 0 || rows[r] >= S) return -1;
+    for (int64_t e = 0; e < (int64_t)H * N * kk; ++e)
+        if (lists[e] < 0 || lists[e] >= N) return -1;
+    lists_ctx_t c = {q, k, v, H, S, lists, kk, rows, out_bf16, out_f64};
+    run_pool(lists_item, &c, n_rows * H, sizeof(double) * (size_t)kk * T, threads);
+    return 0;
+}

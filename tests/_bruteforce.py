@@ -98,3 +98,24 @@ def dense_masked_given_sel(q, k, v, s_t, s_v, s_a, sel):
         p = np.exp(logits - logits.max(axis=1, keepdims=True))
         out[:, h, :] = (p @ V[:, h, :]) / p.sum(axis=1, keepdims=True)
     return out
+
+
+def dense_masked_lists(q, k, v, lists):
+    """Dense attention in which query tile j of head h may only see the key
+    tiles lists[h][j] ([H][N][k], global tile indices): an explicit token-level
+    0/1 mask (-inf where 0) over the S x S logits, one softmax per row, no
+    coarse term.  The whole-sequence SubBlock router hands such lists to the
+    block-sparse kernel.  Returns float64 [S][H][128]."""
+    Q, K, V = (widen(x) for x in (q, k, v))
+    S, H, _ = Q.shape
+    tile_of = np.arange(S) // T
+    alpha = 1.0 / np.sqrt(D)
+    out = np.zeros((S, H, D))
+    for h in range(H):
+        mask = np.zeros((S, S), dtype=bool)
+        for i in range(S):
+            mask[i] = np.isin(tile_of, np.asarray(lists[h][i // T]))
+        logits = np.where(mask, alpha * (Q[:, h, :] @ K[:, h, :].T), -np.inf)
+        p = np.exp(logits - logits.max(axis=1, keepdims=True))
+        out[:, h, :] = (p @ V[:, h, :]) / p.sum(axis=1, keepdims=True)
+    return out
