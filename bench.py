@@ -294,6 +294,41 @@ def subblock_leg(bsv, torch, xd, shape, steps, warmup):
             "steps": steps}
 
 
+def subblock_whole_leg(bsv, torch, xd, shape, steps, warmup):
+    """The whole-sequence SubBlock router (every tile of [text | video | audio]
+    ranks every key tile; sparsity 0.75 -> 288 of 1,166 tiles kept per query
+    tile): router stage alone and the whole forward, HIP events on the
+    current stream."""
+    h, s_t, s_v, s_a = shape
+    sp = SUBBLOCK_SPARSITY
+    out, sel, ws = bsv.alloc_subblock_whole_outputs(h, s_t, s_v, s_a, sp)
+    q, k, v = xd["q"], xd["k"], xd["v"]
+    for _ in range(warmup):
+        bsv.vsa_forward_subblock_whole(q, k, v, s_t, s_v, s_a, sp, out, sel, ws)
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(steps):
+        bsv.vsa_subblock_select_whole(q, k, s_t, s_v, s_a, sp, sel, ws)
+    ev[1].record(stream)
+    for _ in range(steps):
+        bsv.vsa_forward_subblock_whole(q, k, v, s_t, s_v, s_a, sp, out, sel, ws)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    sel_ms = ev[0].elapsed_time(ev[1]) / steps
+    fwd_ms = ev[1].elapsed_time(ev[2]) / steps
+    n = (s_t + s_v + s_a) // TILE
+    kk = sel.shape[2]
+    route_flop = 2.0 * h * (4 * n) ** 2 * D
+    flops = float(h) * n * kk * FLOP_PER_PAIR
+    return {"workload": f"SubBlock router over the whole sequence, same inputs, sparsity {sp} "
+                        f"(k={kk} of {n} tiles per query tile)",
+            "k": kk, "router_ms": sel_ms, "router_fp64_tflops": route_flop / (sel_ms * 1e-3) / 1e12,
+            "ms_per_layer": fwd_ms, "tflops_computed_tiles": flops / (fwd_ms * 1e-3) / 1e12,
+            "steps": steps}
+
+
 def cpu_baseline(x, shape, frac, budget_rows, threads):
     """The oracle (untuned) on a bounded sample: selection + coarse for every
     row, the fine branch for a stratified sample of query rows."""
@@ -465,6 +500,8 @@ def main():
         del xd5, r5
     if not args.no_subblock and args.workload == "10s_56h":
         result["subblock"] = subblock_leg(bsv, torch, xd, shape, args.steps, args.warmup)
+        result["subblock_whole"] = subblock_whole_leg(bsv, torch, xd, shape, args.steps,
+                                                      args.warmup)
     if not args.no_full_layer and args.workload == "10s_56h":
         result["pages_request"] = pages_request(bsv, torch, np, frac, args.steps, args.warmup,
                                                 threads)

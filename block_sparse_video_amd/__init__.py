@@ -20,7 +20,8 @@ __all__ = ["vsa_topk_count", "vsa_workspace_bytes", "vsa_workspace_layout", "vsa
            "vsa_pool_pack", "vsa_select_coarse", "vsa_fine_attention", "forward", "VsaError",
            "status_string", "LIB_PATH", "vsa_subblock_count", "vsa_subblock_workspace_bytes",
            "vsa_forward_subblock", "vsa_subblock_select", "forward_subblock",
-           "vsa_forward_noalloc"]
+           "vsa_forward_noalloc", "vsa_subblock_whole_workspace_bytes",
+           "vsa_forward_subblock_whole", "vsa_subblock_select_whole", "forward_subblock_whole"]
 
 
 def _torch():
@@ -349,4 +350,83 @@ def forward_subblock(q, k, v, text_len, video_len, audio_len, sparsity=0.75, wor
                                           q.device)
     vsa_forward_subblock(q, k, v, text_len, video_len, audio_len, sparsity, out, sel,
                          workspace if workspace is not None else ws, stream)
+    return out, sel
+
+
+# ---------------------------------------------------------------------------
+# SubBlock router over the whole sequence: every tile a query tile and a
+# candidate key tile; selected_tiles is [H][N][k] with global tile indices.
+# ---------------------------------------------------------------------------
+
+def vsa_subblock_whole_workspace_bytes(num_heads: int, text_len: int, video_len: int,
+                                       audio_len: int) -> int:
+    return int(load().vsa_subblock_whole_workspace_bytes(num_heads, text_len, video_len,
+                                                         audio_len))
+
+
+def _whole_k(text_len, video_len, audio_len, sparsity):
+    return vsa_subblock_count(text_len + video_len + audio_len, sparsity)
+
+
+def vsa_forward_subblock_whole(q, k, v, text_len, video_len, audio_len, sparsity, out,
+                               selected_tiles, workspace=None, stream=None):
+    torch = _torch()
+    shp = _shape_args(q, text_len, video_len, audio_len)
+    q, k, v, out = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k"), (v, "v"),
+                                                                    (out, "out")))
+    n = shp[0] // TILE
+    kk = _whole_k(text_len, video_len, audio_len, sparsity)
+    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32,
+                             (shp[1], n, kk) if kk >= 0 else None)
+    workspace = _tensor(workspace, "workspace", torch.uint8)
+    nbytes = workspace.numel() if workspace is not None else 0
+    _on_gpu(q=q, k=k, v=v, out=out, selected_tiles=selected_tiles, workspace=workspace)
+    _check(load().vsa_forward_subblock_whole(_ptr(q), _ptr(k), _ptr(v), shp[1], text_len,
+                                             video_len, audio_len, sparsity, _ptr(out),
+                                             _ptr(selected_tiles), _ptr(workspace), nbytes,
+                                             _stream(stream)), "vsa_forward_subblock_whole")
+
+
+def vsa_subblock_select_whole(q, k, text_len, video_len, audio_len, sparsity, selected_tiles,
+                              workspace, stream=None):
+    torch = _torch()
+    shp = _shape_args(q, text_len, video_len, audio_len)
+    q, k = (_tensor(t, n, torch.bfloat16, shp) for t, n in ((q, "q"), (k, "k")))
+    n = shp[0] // TILE
+    kk = _whole_k(text_len, video_len, audio_len, sparsity)
+    selected_tiles = _tensor(selected_tiles, "selected_tiles", torch.int32,
+                             (shp[1], n, kk) if kk >= 0 else None)
+    workspace = _tensor(workspace, "workspace", torch.uint8)
+    if workspace is None:
+        raise ValueError("vsa_subblock_select_whole needs a workspace")
+    _on_gpu(q=q, k=k, selected_tiles=selected_tiles, workspace=workspace)
+    _check(load().vsa_subblock_select_whole(_ptr(q), _ptr(k), shp[1], text_len, video_len,
+                                            audio_len, sparsity, _ptr(selected_tiles),
+                                            _ptr(workspace), workspace.numel(), _stream(stream)),
+           "vsa_subblock_select_whole")
+
+
+def alloc_subblock_whole_outputs(num_heads, text_len, video_len, audio_len, sparsity,
+                                 device=None):
+    """Allocate (out, selected_tiles, workspace) for vsa_forward_subblock_whole."""
+    torch = _torch()
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    s = text_len + video_len + audio_len
+    kk = _whole_k(text_len, video_len, audio_len, sparsity)
+    wsb = vsa_subblock_whole_workspace_bytes(num_heads, text_len, video_len, audio_len)
+    if kk < 0 or wsb == 0:
+        raise ValueError("bad shape or sparsity")
+    out = torch.empty((s, num_heads, HEAD_DIM), dtype=torch.bfloat16, device=device)
+    sel = torch.empty((num_heads, s // TILE, kk), dtype=torch.int32, device=device)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=device)
+    return out, sel, ws
+
+
+def forward_subblock_whole(q, k, v, text_len, video_len, audio_len, sparsity=0.75, workspace=None,
+                           stream=None):
+    """Convenience wrapper of vsa_forward_subblock_whole (allocates with torch)."""
+    out, sel, ws = alloc_subblock_whole_outputs(q.shape[1], text_len, video_len, audio_len,
+                                                sparsity, q.device)
+    vsa_forward_subblock_whole(q, k, v, text_len, video_len, audio_len, sparsity, out, sel,
+                               workspace if workspace is not None else ws, stream)
     return out, sel

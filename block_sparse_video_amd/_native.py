@@ -29,6 +29,11 @@ SIGNATURES = {
                                           _I64, _I64, _I64, _F32, _P, _P, _P, _P, _SZ, _P]),
     "vsa_forward_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _F32, _P, _P,
                                            _P]),
+    "vsa_subblock_whole_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64]),
+    "vsa_forward_subblock_whole": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I64, _I64, _F32, _P,
+                                                  _P, _P, _SZ, _P]),
+    "vsa_subblock_select_whole": (ctypes.c_int, [_P, _P, _I32, _I64, _I64, _I64, _F32, _P, _P,
+                                                 _SZ, _P]),
     "vsa_subblock_count": (_I32, [_I64, _F32]),
     "vsa_subblock_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64]),
     "vsa_forward_subblock": (ctypes.c_int, [_P, _P, _P, _I32, _I64, _I64, _I64, _F32, _P, _P, _P,

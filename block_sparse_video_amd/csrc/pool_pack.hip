@@ -206,7 +206,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ v, int H,
                                                       int ldh, int n_t, int n_v, int N, int64_t S_t,
                                                       int64_t S_v, int64_t V_t, int64_t V_v,
-                                                      int64_t V_a, PrepArgs pa,
+                                                      int64_t V_a, PrepArgs pa, int pool,
                                                       float* __restrict__ kbar_t,
                                                       float* __restrict__ vbar,
                                                       uint16_t* __restrict__ kpack,
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t* __restrict
         __syncthreads();
     }
     const int u = t - n_t;
-    if (u >= 0 && u < n_v) {
+    if (pool && u >= 0 && u < n_v) {
         const uint16_t* tl = tid < kD ? ktile : vtile;
         const int d = tid & (kD - 1);
         double s = 0.0;
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t* __restrict
 
 hipError_t launch_pool_pack(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const Shape& s, uint8_t* ws, const Layout& L, hipStream_t stream,
-                            const Prep* prep, uint16_t* q_out) {
+                            const Prep* prep, uint16_t* q_out, bool pooled) {
     PrepArgs qa{nullptr, 1, 1, 1, 1, 1, 1}, ka = qa;
     if (prep && prep->gamma_q) {
         qa = PrepArgs{prep->gamma_q, prep->grid[0], prep->grid[1], prep->grid[2],
@@ -325,14 +325,14 @@ hipError_t launch_pool_pack(const uint16_t* q, const uint16_t* k, const uint16_t
                            (double*)(ws + L.qbar64));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-    } else if (s.n_v > 0) {
+    } else if (s.n_v > 0 && pooled) {
         hipLaunchKernelGGL(pool_q_kernel, dim3(s.n_v, (s.H + 7) / 8), dim3(128), 0, stream, q, s.H,
                            s.ldh, s.S_t, s.n_v, s.V_v, (double*)(ws + L.qbar64));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(pack_kv_kernel, dim3(s.N, s.H), dim3(256), 0, stream, k, v, s.H, s.ldh, s.n_t, s.n_v,
-                       s.N, s.S_t, s.S_v, s.V_t, s.V_v, s.V_a, ka, (float*)(ws + L.kbar_t),
+                       s.N, s.S_t, s.S_v, s.V_t, s.V_v, s.V_a, ka, pooled ? 1 : 0, (float*)(ws + L.kbar_t),
                        (float*)(ws + L.vbar), (uint16_t*)(ws + L.kpack), (uint16_t*)(ws + L.vpack));
     return hipGetLastError();
 }

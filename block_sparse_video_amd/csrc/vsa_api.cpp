@@ -67,6 +67,32 @@ int32_t subblock_count(int64_t n_v, float sparsity) {
     return (int32_t)k;
 }
 
+// The whole-sequence SubBlock mode on a relabelled shape: every tile counts
+// as a "video" tile (no text or audio segment, n_v = N), so the router ranks
+// all N tiles for every query tile and the fine kernel walks exactly each
+// query tile's kept list.  No pooled statistics and no coarse term.
+vsa_status whole_shape(int32_t H, int64_t S_t, int64_t S_v, int64_t S_a, float sparsity,
+                       Shape* w) {
+    Shape s;
+    vsa_status st = make_shape(H, S_t, S_v, S_a, &s);
+    if (st != VSA_OK) return st;
+    if (s.N > vsa::kSubblockMaxTiles) return VSA_ERR_TOO_LARGE;
+    const int32_t kk = subblock_count(s.N, sparsity);
+    if (kk < 0) return VSA_ERR_BAD_TOPK;
+    *w = s;
+    w->S_t = 0;
+    w->S_v = s.S;
+    w->S_a = 0;
+    w->n_t = 0;
+    w->n_v = s.N;
+    w->n_a = 0;
+    w->V_t = 0;
+    w->V_v = s.S;
+    w->V_a = 0;
+    w->k = kk;
+    return VSA_OK;
+}
+
 vsa_status check_topk(float frac, Shape* s) {
     const int32_t k = topk_count(s->n_v, frac);
     if (k < 0) return VSA_ERR_BAD_TOPK;
@@ -451,6 +477,64 @@ vsa_status vsa_subblock_select(const void* q, const void* k, int32_t num_heads, 
     if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
     if ((st = check_device()) != VSA_OK) return st;
     return from_hip(vsa::launch_subblock_route((const uint16_t*)q, (const uint16_t*)k, s,
+                                               selected_tiles, (uint8_t*)workspace, L,
+                                               (hipStream_t)stream));
+}
+
+size_t vsa_subblock_whole_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_len,
+                                          int64_t audio_len) {
+    Shape w;
+    if (whole_shape(num_heads, text_len, video_len, audio_len, 0.5f, &w) != VSA_OK) return 0;
+    return vsa::make_layout(w, true, false).total;
+}
+
+vsa_status vsa_forward_subblock_whole(const void* q, const void* k, const void* v,
+                                      int32_t num_heads, int64_t text_len, int64_t video_len,
+                                      int64_t audio_len, float sparsity, void* out,
+                                      int32_t* selected_tiles, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+    if (!q || !k || !v || !out || !selected_tiles) return VSA_ERR_NULL_POINTER;
+    Shape w;
+    vsa_status st = whole_shape(num_heads, text_len, video_len, audio_len, sparsity, &w);
+    if (st != VSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(selected_tiles, 16))
+        return VSA_ERR_MISALIGNED;
+    const Layout L = vsa::make_layout(w, true, false);
+    if (workspace) {
+        if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
+    }
+    if ((st = check_device()) != VSA_OK) return st;
+    if (!workspace) {
+        if ((st = owned_workspace(L.total, &workspace)) != VSA_OK) return st;
+    }
+    hipStream_t strm = (hipStream_t)stream;
+    uint8_t* ws = (uint8_t*)workspace;
+    hipError_t e = vsa::launch_pool_pack((const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
+                                         w, ws, L, strm, nullptr, nullptr, /*pooled=*/false);
+    if (e == hipSuccess)
+        e = vsa::launch_subblock_route((const uint16_t*)q, (const uint16_t*)k, w, selected_tiles,
+                                       ws, L, strm);
+    if (e == hipSuccess)
+        e = vsa::launch_fine_attention((const uint16_t*)q, nullptr, selected_tiles,
+                                       (uint16_t*)out, w, ws, L, strm);
+    return from_hip(e);
+}
+
+vsa_status vsa_subblock_select_whole(const void* q, const void* k, int32_t num_heads,
+                                     int64_t text_len, int64_t video_len, int64_t audio_len,
+                                     float sparsity, int32_t* selected_tiles, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    if (!q || !k || !selected_tiles) return VSA_ERR_NULL_POINTER;
+    Shape w;
+    vsa_status st = whole_shape(num_heads, text_len, video_len, audio_len, sparsity, &w);
+    if (st != VSA_OK) return st;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(selected_tiles, 16))
+        return VSA_ERR_MISALIGNED;
+    const Layout L = vsa::make_layout(w, true, false);
+    if ((st = check_workspace(workspace, workspace_bytes, L)) != VSA_OK) return st;
+    if ((st = check_device()) != VSA_OK) return st;
+    return from_hip(vsa::launch_subblock_route((const uint16_t*)q, (const uint16_t*)k, w,
                                                selected_tiles, (uint8_t*)workspace, L,
                                                (hipStream_t)stream));
 }

@@ -75,10 +75,12 @@ constexpr size_t kSchedBytes = kQueues * 128;
 constexpr int kMaxParts = 4;
 constexpr size_t kPartBytes = (64 * 128 + 128) * sizeof(float);
 
-inline Layout make_layout(const Shape& s, bool subblock = false) {
+// pooled = false: no pooled statistics or coarse regions (a caller that only
+// packs tiles and routes with the SubBlock piece means).
+inline Layout make_layout(const Shape& s, bool subblock = false, bool pooled = true) {
     Layout L;
     size_t off = 0;
-    const size_t hv = (size_t)s.H * (size_t)s.n_v * kD;
+    const size_t hv = pooled ? (size_t)s.H * (size_t)s.n_v * kD : 0;
     L.qbar64 = off; off = align_up(off + hv * sizeof(double));
     L.kbar_t = off; off = align_up(off + hv * sizeof(float));
     L.vbar = off;   off = align_up(off + hv * sizeof(float));
@@ -119,7 +121,8 @@ inline hipError_t ensure_dynamic_lds(const void* kernel, std::atomic<size_t>* al
 // ---- launchers (each enqueues on `stream`, returns the launch status) ----
 hipError_t launch_pool_pack(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                             const Shape& s, uint8_t* ws, const Layout& L, hipStream_t stream,
-                            const Prep* prep = nullptr, uint16_t* q_out = nullptr);
+                            const Prep* prep = nullptr, uint16_t* q_out = nullptr,
+                            bool pooled = true);
 hipError_t launch_select_coarse(const Shape& s, int32_t* sel, uint8_t* ws, const Layout& L,
                                 hipStream_t stream);
 // check_sel: validate every selection row on the device first (rows given by

@@ -246,6 +246,39 @@ vsa_status vsa_subblock_select(const void* q, const void* k, int32_t num_heads, 
                                int32_t* selected_tiles, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/* The SubBlock router over the whole sequence, the page's own reading
+ * (section "How SubBlock Sparse Attention Works": the sequence is divided
+ * into 64-token blocks and every query block ranks the key blocks of its row).
+ * All N = (text_len + video_len + audio_len) / 64 tiles of [text | video |
+ * audio] are query tiles and candidate key tiles alike: the score of the video
+ * mode above (log-sum-exp over the 16 piece pairs, piece means FP32, float64
+ * after them) ranks every key tile of the sequence for every (head, query
+ * tile), the kept count is k = vsa_subblock_count(text_len + video_len +
+ * audio_len, sparsity) (the same rounding to whole groups of 8, over N tiles),
+ * ties go to the lower tile index, and each query tile attends to the keys of
+ * its kept tiles only: nothing is dense, text and audio keys compete like
+ * video keys, and there is no coarse term and no gate.
+ *   selected_tiles: int32 [H][N][k], global tile indices 0..N-1, ascending.
+ * N <= VSA_SUBBLOCK_MAX_VIDEO_TILES (VSA_ERR_TOO_LARGE otherwise).  q, k, v,
+ * out: bf16 [S][H][128] as vsa_forward; every row is a token.  workspace:
+ * NULL (library-owned) or at least vsa_subblock_whole_workspace_bytes(...)
+ * bytes, 256-byte aligned.  Other arguments and errors as vsa_forward. */
+size_t vsa_subblock_whole_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_len,
+                                          int64_t audio_len);
+vsa_status vsa_forward_subblock_whole(const void* q, const void* k, const void* v,
+                                      int32_t num_heads, int64_t text_len, int64_t video_len,
+                                      int64_t audio_len, float sparsity, void* out,
+                                      int32_t* selected_tiles, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* The router stage of vsa_forward_subblock_whole alone (piece means of Q and
+ * K into the workspace, scores and selection into selected_tiles); a caller
+ * workspace of vsa_subblock_whole_workspace_bytes(...) bytes is required. */
+vsa_status vsa_subblock_select_whole(const void* q, const void* k, int32_t num_heads,
+                                     int64_t text_len, int64_t video_len, int64_t audio_len,
+                                     float sparsity, int32_t* selected_tiles, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* The Q, K, V and gate projections that produce this path's inputs (page
  * "UniServe: serving FastH3 at its fastest", section "The FastH3 workload":
  * hidden size 5,376, 56 heads of 128, so each projection maps 5,376 channels

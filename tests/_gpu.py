@@ -147,7 +147,7 @@ def _head_slice(a: np.ndarray, hh: int) -> np.ndarray:
 
 
 def full_size_coverage(x, out, sel, coarse, s_t, s_v, s_a, n_heads=8, every_tile_heads=2,
-                       seed=0, threads=None, rounding_allowance=False, label=""):
+                       seed=0, threads=None, rounding_allowance=False, label="", lists=False):
     """Output checks at a full-size shape, against the oracle on the GPU's own
     index sets:
       - every element of `out` is finite, checked on the device (the output
@@ -159,7 +159,9 @@ def full_size_coverage(x, out, sel, coarse, s_t, s_v, s_a, n_heads=8, every_tile
         and last), the row index varying with the tile.
     x: host bf16 bits {q, k, v, gate} [S][H][128] (gate may be absent: no
     coarse term); sel [H][n_v][k] and coarse [H][n_v][128] as used by the
-    GPU.  Bars as errors_ok (rounding_allowance passed on).  Returns the
+    GPU; lists=True: sel is [H][N][k] per-tile key lists (global indices,
+    the whole-sequence router) and the reference is oracle.fine_lists.  Bars
+    as errors_ok (rounding_allowance passed on).  Returns the
     error summary per group, with the output magnitudes and whether the flat
     max-abs bar held without the rounding allowance."""
     assert bool(torch.isfinite(out).all().item()), f"{label}: non-finite output element"
@@ -169,7 +171,7 @@ def full_size_coverage(x, out, sel, coarse, s_t, s_v, s_a, n_heads=8, every_tile
     gate = x.get("gate")
     if gate is None:
         gate = np.zeros_like(x["q"])
-    if coarse is None:
+    if coarse is None and not lists:
         coarse = np.zeros((h, n_v, D))
     got_all = from_dev_bits(out)
     rng = np.random.default_rng(seed)
@@ -189,10 +191,15 @@ def full_size_coverage(x, out, sel, coarse, s_t, s_v, s_a, n_heads=8, every_tile
     summary = {}
     for kind, hh, rows in plans:
         rows = rows.astype(np.int64)
-        _, ref = oracle.fine(_head_slice(x["q"], hh), _head_slice(x["k"], hh),
-                             _head_slice(x["v"], hh), _head_slice(gate, hh), s_t, s_v, s_a,
-                             sel[hh:hh + 1] if n_v else None,
-                             coarse[hh:hh + 1] if n_v else None, rows, threads=threads)
+        if lists:
+            _, ref = oracle.fine_lists(_head_slice(x["q"], hh), _head_slice(x["k"], hh),
+                                       _head_slice(x["v"], hh), sel[hh:hh + 1], rows,
+                                       threads=threads)
+        else:
+            _, ref = oracle.fine(_head_slice(x["q"], hh), _head_slice(x["k"], hh),
+                                 _head_slice(x["v"], hh), _head_slice(gate, hh), s_t, s_v, s_a,
+                                 sel[hh:hh + 1] if n_v else None,
+                                 coarse[hh:hh + 1] if n_v else None, rows, threads=threads)
         got = got_all[rows, hh:hh + 1]
         e = output_errors(got, ref)
         assert errors_ok(e, rounding_allowance), (label, kind, hh, e)

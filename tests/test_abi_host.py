@@ -269,3 +269,38 @@ def test_noalloc_limit_is_one_head_of_workspace():
                if bsv.vsa_workspace_bytes(1, 64, 64 * n, 64) <= cap)
     assert noalloc(h=1, vid=64 * n_ok) not in (TOO_LARGE, SHAPE, UNALIGNED)
     assert noalloc(h=1, vid=64 * (n_ok + 7)) == TOO_LARGE
+
+
+def test_subblock_whole_validation():
+    lib = _native.load()
+    f = lib.vsa_forward_subblock_whole
+    args = dict(q=FAKE, k=FAKE, v=FAKE, h=2, t=64, vid=640, au=64, sp=0.75, out=FAKE, sel=FAKE,
+                ws=FAKE, wsb=1 << 40)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["q"], a["k"], a["v"], a["h"], a["t"], a["vid"], a["au"], a["sp"], a["out"],
+                 a["sel"], a["ws"], a["wsb"], None)
+    assert call(q=None) == NULLP
+    assert call(sel=None) == NULLP
+    assert call(h=0) == SHAPE
+    assert call(vid=100) == UNALIGNED
+    assert call(sp=1.0) == TOPK
+    # N counts every tile: 5,119 video + 2 tiles passes the router's 5,120 limit
+    assert call(vid=64 * 5119) == TOO_LARGE
+    assert call(out=FAKE + 2) == MISALIGNED
+    assert call(sel=FAKE + 4) == MISALIGNED
+    assert call(wsb=bsv.vsa_subblock_whole_workspace_bytes(2, 64, 640, 64) - 256) == WORKSPACE
+    g = lib.vsa_subblock_select_whole
+    assert g(FAKE, FAKE, 2, 64, 640, 64, 0.75, FAKE, None, 1 << 40, None) == WORKSPACE
+    assert g(FAKE, FAKE, 2, 64, 640, 64, 0.75, None, FAKE, 1 << 40, None) == NULLP
+
+
+def test_subblock_whole_workspace_and_count():
+    # kpack + vpack of every tile, the 1 KiB counters, then the two piece-mean regions
+    h, n = 56, 1166
+    n_c = (n + 3) // 4
+    total = bsv.vsa_subblock_whole_workspace_bytes(h, 1024, 72576, 1024)
+    assert total == 2 * h * n * 16384 + 1024 + 2 * h * n_c * 8192
+    assert bsv.vsa_subblock_count(74624, 0.75) == 288   # the whole-sequence kept count
+    assert bsv.vsa_subblock_whole_workspace_bytes(1, 64, 64 * 5119, 64) == 0
