@@ -1,5 +1,5 @@
 // pool_pack.hip -- stage 1 of the VSA forward on gfx950: FP32 tile pooling of
-// Q, K, V over the video tiles, and packing of V tiles for the attention stage.
+// Q, K, V over the video tiles, and packing of K and V tiles for the attention stage.
 //
 // Page "UniServe: serving FastH3 at its fastest", section "Fused attention
 // preprocessing": the preprocessing pass pools tiles into FP32 statistics and
