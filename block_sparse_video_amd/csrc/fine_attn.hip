@@ -66,7 +66,7 @@ struct FineArgs {
     const int32_t* sel;
     const float* coarse;
     uint16_t* out;
-    uint32_t* sched;    // kQueues work-queue counters, 32 words apart, zero at launch
+    uint32_t* sched;    // kQueues + 2 work-queue counters, 32 words apart, zero at launch
     float* partial;     // dense parts: [dense unit][part][64 x 128 O, 64 l, 64 reference]
     int parts;          // key-list parts per dense unit (1: no split)
     int check_sel;      // nonzero: validate each selection row before use (caller-supplied rows)
@@ -76,87 +76,93 @@ struct FineArgs {
 };
 
 // Work queues.  The kernel is persistent: one workgroup per wavefront slot,
-// each taking units (head h, query tile j) from kQueues queues until all are
-// empty.  Queue x is meant for XCD x and holds, in this order,
-//  - video units: with an even head count, XCDs 0-3 take the even heads' and
-//    XCDs 4-7 the odd heads', each group in head-major order dealt
-//    round-robin to its four XCDs.  Two heads are then in flight at a time,
-//    each pulled into four L2s instead of eight while both stay within the
-//    last-level cache, and the resident units of a head start together and
-//    sweep their ascending key lists at the same pace.  With an odd head
-//    count the video units are dealt round-robin to all eight queues;
-//  - then a contiguous 1/8 share of the dense (text/audio query) items,
-//    ordered by head, then key-list part, then query tile.  A dense unit's
-//    list is every tile (~4.5x a video unit's), so it is walked as P parts
-//    of about a video unit's length and the parts are combined afterwards;
-//    the parts of one head share one L2 and sweep their key ranges in step.
-//    (Dense items first measured 15-20% slower: the video units then start
-//    unevenly and lose their lockstep.)
+// each taking units (head h, query tile j) from shared counters until every
+// queue is empty.  Two kinds of queue:
+//  - video queues, one per head group: with an even head count, XCDs 0-3
+//    take the even heads' video units and XCDs 4-7 the odd heads', from one
+//    counter per group, in head-major order, query tiles ascending.  Two
+//    heads are then in flight at a time, each pulled into four L2s instead
+//    of eight while both stay within the last-level cache, and the four
+//    XCDs of a group always work on the same head: an XCD that runs slower
+//    simply takes fewer units.  (With one queue per XCD the XCDs of a group
+//    drift apart on inputs whose selections cluster around each query tile:
+//    a lagging XCD's units slow down further and the group ends up spread
+//    over several heads.)  With an odd head count all video units are in
+//    one queue for all eight XCDs;
+//  - dense queues, one per XCD: a contiguous 1/8 share of the dense
+//    (text/audio query) items, ordered by head, then key-list part, then
+//    query tile.  A dense unit's list is every tile (~4.5x a video unit's),
+//    so it is walked as P parts of about a video unit's length and the parts
+//    are combined afterwards; the parts of one head share one L2 and sweep
+//    their key ranges in step.  They follow the video units (dense items
+//    first measured 15-20% slower: the video units then start unevenly).
+// Counters: dense queue x at word 32x, video queue G at word 32 (8 + G).
+constexpr int kVideoQueue = kQueues;  // queue index of head group 0's video queue
+
 __device__ __forceinline__ int dense_begin(int D, int x) { return (int)(((int64_t)D * x) / kQueues); }
 
-__device__ __forceinline__ int video_count(int H, int n_v, int x) {
-    if ((H & 1) == 0) {
-        const int vg = (H >> 1) * n_v, m = x & 3;
-        return vg > m ? (vg - m + 3) / 4 : 0;
-    }
-    const int v = H * n_v;
-    return v > x ? (v - x + kQueues - 1) / kQueues : 0;
+// Units in queue q (dense: q < 8; video: q = kVideoQueue + G).
+__device__ __forceinline__ int queue_count(int H, int n_v, int D, int q) {
+    if (q < kQueues) return dense_begin(D, q + 1) - dense_begin(D, q);
+    const int G = q - kVideoQueue;
+    if ((H & 1) == 0) return (H >> 1) * n_v;
+    return G == 0 ? H * n_v : 0;
 }
 
-// Unit i of queue x -> (h, j) and, for a dense unit, its key-list part p.
-__device__ __forceinline__ void queue_unit(int H, int n_t, int n_v, int n_a, int P, int x, int i,
+// Unit i of queue q -> (h, j) and, for a dense unit, its key-list part p.
+__device__ __forceinline__ void queue_unit(int H, int n_t, int n_v, int n_a, int P, int q, int i,
                                            int& h, int& j, int& p) {
     const int n_h = n_t + n_a;
-    const int D = H * P * n_h;
-    const int d0 = dense_begin(D, x);
-    const int nvx = video_count(H, n_v, x);
-    const bool dense = i >= nvx;
-    const int r = dense ? i - nvx : i;
     p = 0;
-    if (dense) {
-        const int item = d0 + r;
+    if (q < kQueues) {
+        const int item = dense_begin(H * P * n_h, q) + i;
         const int hp = item / n_h;  // head-major, then part, then query tile
         const int t = item - hp * n_h;
         h = hp / P;
         p = hp - h * P;
         j = t < n_t ? t : n_v + t;
-    } else if ((H & 1) == 0) {
-        const int ug = (x & 3) + 4 * r;
-        const int hh = ug / n_v;
-        h = 2 * hh + (x >> 2);
-        j = n_t + (ug - hh * n_v);
     } else {
-        const int v = x + kQueues * r;
-        h = v / n_v;
-        j = n_t + (v - h * n_v);
+        const int hh = i / n_v;
+        h = (H & 1) == 0 ? 2 * hh + (q - kVideoQueue) : hh;
+        j = n_t + (i - hh * n_v);
     }
 }
 
-// A workgroup first drains the queue of the XCD it runs on (read from the
-// hardware), then those of the other XCDs of its head group, then the rest:
-// XCDs that run faster take units from slower ones, and no slot idles while
-// work remains.  Returns the index of the next unit in queue `x`, or -1 when
-// every queue is empty.  `empty` collects the queues this workgroup has seen
-// exhausted.
+// Queue s of the order a workgroup on XCD xcc tries: its group's video
+// queue (the only one with an odd head count), its own dense queue, the other dense queues of its group, then the
+// other group's video queue and the remaining dense queues, so that faster
+// XCDs take units from slower ones and no slot idles while work remains.
+__device__ __forceinline__ int queue_order(int H, int xcc, int s) {
+    const int G = (H & 1) ? 0 : (xcc >> 2);  // one video queue for all XCDs with odd H
+    if (s == 0) return kVideoQueue + G;
+    if (s <= 4) return (xcc & 4) | ((xcc + s - 1) & 3);
+    if (s == 5) return kVideoQueue + (G ^ 1);
+    return (~xcc & 4) | ((xcc + s - 6) & 3);
+}
+
+// Returns the index of the next unit in queue `q`, or -1 when every queue is
+// empty.  `empty` collects the queues this workgroup has seen exhausted.
 __device__ __forceinline__ int next_unit(uint32_t* sched, int H, int n_t, int n_v, int n_a, int P,
-                                         int xcc, uint32_t& empty, int& x) {
+                                         int xcc, uint32_t& empty, int& q) {
     const int D = H * P * (n_t + n_a);
 #pragma unroll 1
-    for (int s = 0; s < kQueues; ++s) {
-        x = ((xcc + (s & 4)) & 4) | ((xcc + s) & 3);
-        if ((empty >> x) & 1u) continue;
-        const int count = dense_begin(D, x + 1) - dense_begin(D, x) + video_count(H, n_v, x);
+    for (int s = 0; s < kQueues + 2; ++s) {
+        q = queue_order(H, xcc, s);
+        if ((empty >> q) & 1u) continue;
+        const int count = queue_count(H, n_v, D, q);
         uint32_t i = 0;
-        if (threadIdx.x == 0) i = atomicAdd(sched + 32 * x, 1u);
-        i = __builtin_amdgcn_readfirstlane(i);
-        if ((int)i < count) return (int)i;
-        empty |= 1u << x;
+        if (count > 0) {
+            if (threadIdx.x == 0) i = atomicAdd(sched + 32 * q, 1u);
+            i = __builtin_amdgcn_readfirstlane(i);
+            if ((int)i < count) return (int)i;
+        }
+        empty |= 1u << q;
     }
     return -1;
 }
 
 __global__ void clear_sched_kernel(uint32_t* sched) {
-    for (int i = threadIdx.x; i < 32 * kQueues; i += blockDim.x) sched[i] = 0u;
+    for (int i = threadIdx.x; i < 32 * (kQueues + 2); i += blockDim.x) sched[i] = 0u;
 }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
