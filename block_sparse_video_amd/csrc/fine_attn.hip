@@ -13,7 +13,8 @@
 // One wavefront computes one work unit (head h, query tile j): 64 query rows
 // against every key tile of the unit's list, walked as half-tiles of 32 keys.
 // The kernel is persistent: each single-wavefront workgroup takes units from
-// per-XCD work queues (counters in the workspace) until every queue is empty.
+// shared work queues (one per head group of XCDs for video units, one per XCD
+// for text/audio units; counters in the workspace) until every queue is empty.
 // Every K/V element a unit needs is used by that wavefront only, so the
 // wavefront streams its operands into a private 40 KiB LDS ring (three K
 // slots, two V slots) with global_load_lds_dwordx4 and needs no barriers.

@@ -66,9 +66,11 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 // the 160 KiB of LDS, and the wavefront top-k holds 80 keys per lane.
 constexpr int kSubblockMaxTiles = 5120;
 
-// Fine-attention work queues: one counter per XCD, each on its own 128-byte line.
+// Fine-attention work queues: kQueues dense (text/audio unit) queues, one per
+// XCD, then one video-unit queue per head group of four XCDs; each counter on
+// its own 128-byte line.
 constexpr int kQueues = 8;
-constexpr size_t kSchedBytes = (kQueues + 2) * 128;  // 8 dense queues + 2 video queues
+constexpr size_t kSchedBytes = (kQueues + 2) * 128;
 // A dense (text/audio query) unit's key list is split into at most this many
 // parts; one part's record is 64 x 128 unnormalised outputs, 64 denominators
 // and 64 softmax references, float32.
