@@ -50,6 +50,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 64;
 // s_getreg_b32 operand for HW_REG_XCC_ID (register 20, bits 0..31): the XCD
@@ -412,10 +413,13 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         // Q^T fragments (B operand of S^T = K Q^T): query l32 of block qb, dims 16s + 8g .. +7
         bf16x8 qf[2][8];
 #pragma unroll
+        // Q, the gate and the output rows are each touched once: non-temporal
+        // accesses keep them from displacing K/V lines in the L2
         for (int qb = 0; qb < 2; ++qb) {
             const uint16_t* qp = a.q + ((int64_t)j * kT + 32 * qb + l32) * rs + (int64_t)h * kD + 8 * g;
 #pragma unroll
-            for (int s8 = 0; s8 < 8; ++s8) qf[qb][s8] = *(const bf16x8*)(qp + 16 * s8);
+            for (int s8 = 0; s8 < 8; ++s8)
+                qf[qb][s8] = __builtin_nontemporal_load((const bf16x8*)(qp + 16 * s8));
         }
         wait_vmcnt(0);  // Q is resident before the ring starts counting loads
         // padding query rows (past the tile's token rows) attend with zeros and
@@ -668,7 +672,10 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
         if (gated) {
             const uint16_t* gp = a.gate + ((int64_t)j * kT + (lane >> 4)) * rs + (int64_t)h * kD + 8 * c16;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) gw[i] = *(const uint4*)(gp + 4 * i * rs);
+            for (int i = 0; i < 16; ++i) {
+                const u32x4 t4 = __builtin_nontemporal_load((const u32x4*)(gp + 4 * i * rs));
+                gw[i] = make_uint4(t4[0], t4[1], t4[2], t4[3]);
+            }
             const float* cp = a.coarse + ((int64_t)h * a.n_v + u) * kD + 8 * c16;
             cv0 = *(const float4*)cp;
             cv1 = *(const float4*)(cp + 4);
@@ -732,7 +739,8 @@ __global__ __launch_bounds__(kThreads) void fine_attn_kernel(FineArgs a) {
                     y[2 * e + 1] += sigmoidf(__uint_as_float(gwv[e] & 0xFFFF0000u)) * cv[2 * e + 1];
                 }
             }
-            *(bf16x8*)(a.out + grow * rs + (int64_t)h * kD + 8 * c) = __builtin_convertvector(y, bf16x8);
+            __builtin_nontemporal_store(__builtin_convertvector(y, bf16x8),
+                                        (bf16x8*)(a.out + grow * rs + (int64_t)h * kD + 8 * c));
         }
         // the next unit's copies overwrite the staging area
         wait_lgkm();
