@@ -230,64 +230,157 @@ __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __rest
 // agree with the sequential chain, about 70% with the others.)
 // Operand layout (lane l): A[row l % 16][k l / 16], B[k l / 16][col l % 16];
 // result D[row l / 16 + 4 v][col l % 16] in element v.
+//
+// The 16 score rows are kept in LDS as float32 (74 KiB at 1,134 tiles, so two
+// workgroups share a CU and one's top-k overlaps the other's matrix work).
+// Rounding to float32 is monotone, so a float32 score above the row's k-th
+// largest float32 value belongs to a float64 score above every float64 score
+// at or below it: the selection is exact except inside the band of scores
+// whose float32 value equals the k-th.  When that band holds more entries
+// than are still to be taken, their float64 scores are recomputed (the same
+// d-order chain, with the same exact products) and ranked among themselves,
+// ties to the lower index.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsM = 16;   // query rows per workgroup: the instruction's M
 constexpr int kWavesM = 8;   // 512 threads
+constexpr int kSlotsM = 20;  // keys per lane in the top-k (n_v <= 64 * 20)
 
-// LDS row pitch in doubles: at least n_v, 4 modulo 32, so that the 16 rows
-// of one operand read fall on 8 different groups of banks.
-__host__ __device__ inline int mfma_pitch(int n_v) { return ((n_v + 27) / 32) * 32 + 4; }
+// LDS row pitch in floats: at least n_v, 8 modulo 64, so that the 16 rows of
+// one operand read fall on 8 different groups of banks.
+__host__ __device__ inline int mfma_pitch(int n_v) { return ((n_v + 55) / 64) * 64 + 8; }
 
 __device__ __forceinline__ f64x4 mfma64(double a, double b, f64x4 c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(512) void select_coarse_mfma_kernel(
+// Order-preserving map of a float32 to uint32 (key 0 is never a finite score).
+__device__ __forceinline__ uint32_t order_key32(float x) {
+    const uint32_t b = __float_as_uint(x);
+    return (b >> 31) ? ~b : (b | 0x80000000u);
+}
+
+// The kk-th largest of the keys a wavefront holds (kk >= 1, at least kk keys
+// nonzero; zero keys are absent), by bisection on the key value; `gt`
+// returns the number of keys above it.
+template <typename Key, int NS>
+__device__ __forceinline__ Key kth_largest(const Key (&kv)[NS], uint32_t kk, uint32_t& gt) {
+    Key kmin = ~(Key)0, kmax = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        kmax = kv[i] > kmax ? kv[i] : kmax;
+        kmin = (kv[i] != 0 && kv[i] < kmin) ? kv[i] : kmin;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const Key a = __shfl_xor(kmin, off), b = __shfl_xor(kmax, off);
+        kmin = a < kmin ? a : kmin;
+        kmax = b > kmax ? b : kmax;
+    }
+    auto count_ge = [&](Key th) -> uint32_t {
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) c += (uint32_t)__popcll(__ballot(kv[i] >= th));
+        return c;
+    };
+    // the answer is the largest T with count_ge(T) >= kk, a key value in
+    // [kmin, kmax]; invariant: count_ge(lo) >= kk and the answer is <= hi
+    Key lo = kmin, hi = kmax;
+    while (lo < hi) {
+        const Key mid = lo + (Key)((hi - lo + 1) >> 1);
+        if (count_ge(mid) >= kk) lo = mid;
+        else hi = mid - 1;
+    }
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) c += (uint32_t)__popcll(__ballot(kv[i] > lo));
+    gt = c;
+    return lo;
+}
+
+// Selection of one row whose band (float32 score equal to the k-th largest,
+// t32) holds more entries than the `need` still to take: the band's float64
+// scores are recomputed as the d-order chain of exact products (the value the
+// matrix instruction produced), and the row's selection is every key above
+// t32 plus the band's `need` best by (float64 score desc, index asc), written
+// in ascending index order.  Kept out of line: rows whose band is exactly
+// what is needed (nearly all) never run it.
+__device__ __noinline__ void emit_band_resolved(const float* row, const double* qrow,
+                                                const float* kb_h, int n_v, int k, uint32_t t32,
+                                                uint32_t need, int lane, int32_t* out) {
+    uint64_t kb64[kSlotsM];
+#pragma unroll
+    for (int i = 0; i < kSlotsM; ++i) {
+        const int w = lane + 64 * i;
+        kb64[i] = 0ull;
+        if (w < n_v && order_key32(row[w]) == t32) {
+            double s = 0.0;
+            for (int d = 0; d < kD; ++d) s = __builtin_fma(qrow[d], (double)kb_h[(int64_t)d * n_v + w], s);
+            kb64[i] = order_key(s + 0.0);
+        }
+    }
+    uint32_t gt64;
+    const uint64_t t64 = kth_largest(kb64, need, gt64);
+    const uint32_t need64 = need - gt64;  // band entries equal to t64 to take, lowest index first
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    uint32_t outc = 0, eqseen = 0;
+#pragma unroll
+    for (int i = 0; i < kSlotsM; ++i) {
+        const int w = lane + 64 * i;
+        const bool valid = w < n_v;
+        const uint32_t key = valid ? order_key32(row[w]) : 0u;
+        const bool eq64 = kb64[i] != 0ull && kb64[i] == t64;
+        const uint64_t em = __ballot(eq64);
+        const uint32_t erank = eqseen + (uint32_t)__popcll(em & lt_mask);
+        const bool take = key > t32 || kb64[i] > t64 || (eq64 && erank < need64);
+        const uint64_t tm = __ballot(take);
+        const uint32_t pos = outc + (uint32_t)__popcll(tm & lt_mask);
+        if (take && valid && pos < (uint32_t)k) out[pos] = w;
+        outc += (uint32_t)__popcll(tm);
+        eqseen += (uint32_t)__popcll(em);
+    }
+}
+
+__global__ __launch_bounds__(512, 4) void select_coarse_mfma_kernel(
     const double* __restrict__ qbar64, const float* __restrict__ kbar_t,
     const float* __restrict__ vbar, int n_v, int k, int pitch, float alpha,
     int32_t* __restrict__ sel, float* __restrict__ coarse) {
     extern __shared__ __align__(16) unsigned char smem[];
-    double* sc = (double*)smem;               // [16][pitch] scores, later softmax weights
-    double* rowsum = sc + kRowsM * pitch;     // [16]
+    float* sc = (float*)smem;                          // [16][pitch] scores, later weights
+    double* rowsum = (double*)(sc + kRowsM * pitch);   // [16]
 
     const int h = blockIdx.y;
     const int u0 = blockIdx.x * kRowsM;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int lr = lane & 15, lk = lane >> 4;
+    const float* kb_h = kbar_t + (int64_t)h * kD * n_v;
 
     // ---- scores S[r][w] = sum_d Qbar[u0 + r][d] Kbar[w][d] -----------------
     // wave wv computes the 16-key blocks wv, wv + 8, ...; the A operands (this
     // workgroup's query rows, all 32 dimension groups) are loaded once, and
-    // the pooled K of a wave's next block is requested while the current one
-    // is multiplied (one chain of 32 MFMAs per block, in d order).
+    // each block is one chain of 32 MFMAs, in d order.
     {
         double qa[32];
         const double* qrow = qbar64 + ((int64_t)h * n_v + min(u0 + lr, n_v - 1)) * kD + lk;
 #pragma unroll
         for (int ds = 0; ds < 32; ++ds) qa[ds] = qrow[4 * ds];
-        const float* kb = kbar_t + (int64_t)h * kD * n_v + (int64_t)lk * n_v;
+        const float* kb = kb_h + (int64_t)lk * n_v;
         const int nblk = (n_v + 15) / 16;
-        float kc[32], kn[32];
-        auto load_block = [&](int b) {
-            const int w = min(16 * b + lr, n_v - 1);
-#pragma unroll
-            for (int ds = 0; ds < 32; ++ds) kn[ds] = kb[(int64_t)4 * ds * n_v + w];
-        };
-        if (wv < nblk) load_block(wv);
 #pragma unroll 1
         for (int b = wv; b < nblk; b += kWavesM) {
+            const int w = min(16 * b + lr, n_v - 1);
+            float kc[32];
 #pragma unroll
-            for (int ds = 0; ds < 32; ++ds) kc[ds] = kn[ds];
-            if (b + kWavesM < nblk) load_block(b + kWavesM);
+            for (int ds = 0; ds < 32; ++ds) kc[ds] = kb[(int64_t)4 * ds * n_v + w];
             f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
             for (int ds = 0; ds < 32; ++ds) acc = mfma64(qa[ds], (double)kc[ds], acc);
             // x + 0.0 turns -0.0 into +0.0, so equal scores have equal keys
             if (16 * b + lr < n_v)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) sc[(lk + 4 * v) * pitch + 16 * b + lr] = acc[v] + 0.0;
+                for (int v = 0; v < 4; ++v)
+                    sc[(lk + 4 * v) * pitch + 16 * b + lr] = (float)(acc[v] + 0.0);
         }
     }
     __syncthreads();
@@ -296,22 +389,51 @@ __global__ __launch_bounds__(512) void select_coarse_mfma_kernel(
 #pragma unroll 1
     for (int t = 0; t < 2; ++t) {
         const int r = wv + kWavesM * t;
-        if (u0 + r >= n_v) continue;
-        double* row = sc + r * pitch;
-        uint32_t remaining = (uint32_t)k;
-        const uint64_t kth = kth_key_bisect<20>(row, n_v, k, lane, remaining);
-        emit_topk(row, n_v, k, kth, remaining, lane, sel + ((int64_t)h * n_v + u0 + r) * k);
-        double m = -INFINITY;
-        for (int w = lane; w < n_v; w += 64) m = fmax(m, row[w]);
+        const int u = u0 + r;
+        if (u >= n_v) continue;
+        float* row = sc + r * pitch;
+        uint32_t kv[kSlotsM];
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+        for (int i = 0; i < kSlotsM; ++i) {
+            const int w = lane + 64 * i;
+            kv[i] = w < n_v ? order_key32(row[w]) : 0u;
+        }
+        uint32_t gt32;
+        const uint32_t t32 = kth_largest(kv, (uint32_t)k, gt32);
+        const uint32_t need = (uint32_t)k - gt32;  // entries still to take from the band
+        uint32_t band = 0;
+#pragma unroll
+        for (int i = 0; i < kSlotsM; ++i) band += (uint32_t)__popcll(__ballot(kv[i] == t32));
+        int32_t* out = sel + ((int64_t)h * n_v + u) * k;
+        if (band > need) {
+            // band wider than what is left to take: rank it by float64 score
+            emit_band_resolved(row, qbar64 + ((int64_t)h * n_v + u) * kD, kb_h, n_v, k, t32,
+                               need, lane, out);
+        } else {
+            // keys above t32 and the whole band, in ascending index order
+            const uint64_t lt_mask = (1ull << lane) - 1ull;
+            uint32_t outc = 0;
+#pragma unroll
+            for (int i = 0; i < kSlotsM; ++i) {
+                const int w = lane + 64 * i;
+                const bool take = kv[i] >= t32;
+                const uint64_t tm = __ballot(take);
+                const uint32_t pos = outc + (uint32_t)__popcll(tm & lt_mask);
+                if (take && w < n_v && pos < (uint32_t)k) out[pos] = w;
+                outc += (uint32_t)__popcll(tm);
+            }
+        }
+        float m = -INFINITY;
+        for (int w = lane; w < n_v; w += 64) m = fmaxf(m, row[w]);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
         double lsum = 0.0;
         for (int w = lane; w < n_v; w += 64) {
-            const float p = __expf((float)((row[w] - m) * (double)alpha));
-            row[w] = (double)p;
+            const float p = __expf((float)(((double)row[w] - (double)m) * (double)alpha));
+            row[w] = p;
             lsum += (double)p;
         }
-        for (int w = n_v + lane; w < pitch; w += 64) row[w] = 0.0;  // padding: weight 0
+        for (int w = n_v + lane; w < pitch; w += 64) row[w] = 0.0f;  // padding: weight 0
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) lsum += __shfl_xor(lsum, off);
         if (lane == 0) rowsum[r] = lsum;
@@ -324,19 +446,19 @@ __global__ __launch_bounds__(512) void select_coarse_mfma_kernel(
     // compute garbage that is never stored.
     {
         const float* vb = vbar + (int64_t)h * n_v * kD + 16 * wv + lr;
-        const double* prow = sc + lr * pitch + lk;
+        const float* prow = sc + lr * pitch + lk;
         const int nks = (n_v + 3) / 4;
         f64x4 c0 = {0.0, 0.0, 0.0, 0.0}, c1 = c0;
         constexpr int G = 16;  // key groups per batch; the next batch is requested
                                // while the current one is multiplied
         float vv[G], vn[G];
         double pa[G], pn[G];
-        auto load_batch = [&](int ks0, float (&v)[G], double (&p)[G]) {
+        auto load_batch = [&](int ks0, float (&v)[G], double (&pw)[G]) {
 #pragma unroll
             for (int i = 0; i < G; ++i) {
                 const int ks = min(ks0 + i, nks - 1);
                 v[i] = vb[(int64_t)min(4 * ks + lk, n_v - 1) * kD];
-                p[i] = ks0 + i < nks ? prow[4 * ks] : 0.0;
+                pw[i] = ks0 + i < nks ? (double)prow[4 * ks] : 0.0;
             }
         };
         load_batch(0, vn, pn);
@@ -387,13 +509,13 @@ constexpr size_t kSelectLdsMax = 160 * 1024;
 
 size_t select_lds_bytes(int R, int ldw) { return (size_t)R * ldw * 8 + 4 * 256 * 4 + (size_t)R * 8; }
 
-size_t select_mfma_lds_bytes(int n_v) { return ((size_t)kRowsM * mfma_pitch(n_v) + kRowsM) * 8; }
+size_t select_mfma_lds_bytes(int n_v) { return (size_t)kRowsM * mfma_pitch(n_v) * 4 + kRowsM * 8; }
 
 hipError_t launch_select_coarse(const Shape& s, int32_t* sel, uint8_t* ws, const Layout& L,
                                 hipStream_t stream) {
     // rows of up to 64 * 20 keys whose 16 float64 rows fit the LDS: the
     // matrix-core kernel
-    if (s.n_v <= 64 * 20 && select_mfma_lds_bytes(s.n_v) <= kSelectLdsMax) {
+    if (s.n_v <= 64 * kSlotsM && select_mfma_lds_bytes(s.n_v) <= kSelectLdsMax) {
         static std::atomic<size_t> lds_allowed[kMaxDevices];
         const size_t lds = select_mfma_lds_bytes(s.n_v);
         hipError_t e = ensure_dynamic_lds((const void*)select_coarse_mfma_kernel, lds_allowed, lds);

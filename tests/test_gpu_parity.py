@@ -167,6 +167,40 @@ def test_paired_key_tiles_tie_at_the_boundary():
     assert ref["k"] == 21
 
 
+def test_float32_ties_decided_in_float64():
+    """K tiles equal in pairs except for one bf16 step in dimension 0 of one
+    row, and every query row weights dimension 0 by 2^-30: the two scores of a
+    pair differ by about 2^-44, so they round to the same float32 but not to
+    the same float64, and with k odd the selection boundary of every row falls
+    inside such a pair.  The larger float64 score must win, whichever index it
+    has.  Selection must match the oracle exactly."""
+    announce("float32-tied pairs: h=2 tiles=(1,70,1) frac=0.3 (k=21)")
+    h, s_t, n_v, s_a = 2, 64, 70, 64
+    s_v = n_v * T
+    x = synth.vsa_inputs(23, h, s_t, s_v, s_a)
+    kp, qp = x["k"].copy(), x["q"].copy()
+    qp[..., 0] = synth.f32_to_bf16_bits(np.array(2.0 ** -30, np.float32))
+    rng = np.random.default_rng(23)
+    for w in range(0, n_v, 2):
+        a = s_t + w * T
+        kp[a + T: a + 2 * T] = kp[a: a + T]
+        bits = kp[a + T, :, 0].astype(np.int32)
+        step = 1 if rng.random() < 0.5 else -1  # the next or the previous bf16 value
+        step = np.where((bits & 0x7FFF) == 0, 1, step)  # never step below a zero
+        kp[a + T, :, 0] = (bits + step).astype(np.uint16)
+    assert np.all(np.isfinite(G.widen(kp)))
+    ref, *_ = full_check(dict(x, q=qp, k=kp), s_t, s_v, s_a, 0.3, exempt_ok=False)
+    assert ref["k"] == 21
+    # the construction does what it says: the 21st and 22nd largest float64
+    # scores differ, and round to the same float32
+    tied = 0
+    for hh in range(h):
+        for u in range(n_v):
+            s = np.sort(oracle.row_scores(ref["qbar"], ref["kbar"], hh, u))[::-1]
+            tied += int(s[20] != s[21] and np.float32(s[20]) == np.float32(s[21]))
+    assert tied >= n_v, tied
+
+
 @pytest.mark.slow
 def test_long_rows_use_the_radix_select():
     """n_v = 1,300 video tiles: rows too long for the register bisection go
