@@ -303,9 +303,9 @@ __device__ __forceinline__ Key kth_largest(const Key (&kv)[NS], uint32_t kk, uin
 // scores are recomputed as the d-order chain of exact products (the value the
 // matrix instruction produced), and the row's selection is every key above
 // t32 plus the band's `need` best by (float64 score desc, index asc), written
-// in ascending index order.  Kept out of line: rows whose band is exactly
-// what is needed (nearly all) never run it.
-__device__ __noinline__ void emit_band_resolved(const float* row, const double* qrow,
+// in ascending index order.  Rows whose band is exactly what is needed
+// (nearly all) never run it.
+__device__ __forceinline__ void emit_band_resolved(const float* row, const double* qrow,
                                                 const float* kb_h, int n_v, int k, uint32_t t32,
                                                 uint32_t need, int lane, int32_t* out) {
     uint64_t kb64[kSlotsM];
