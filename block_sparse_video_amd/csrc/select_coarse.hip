@@ -260,6 +260,14 @@ __device__ __forceinline__ uint32_t order_key32(float x) {
     return (b >> 31) ? ~b : (b | 0x80000000u);
 }
 
+__device__ __forceinline__ uint32_t uniform_key(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+__device__ __forceinline__ uint64_t uniform_key(uint64_t x) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+}
+
 // The kk-th largest of the keys a wavefront holds (kk >= 1, at least kk keys
 // nonzero; zero keys are absent), by bisection on the key value; `gt`
 // returns the number of keys above it.
@@ -277,6 +285,10 @@ __device__ __forceinline__ Key kth_largest(const Key (&kv)[NS], uint32_t kk, uin
         kmin = a < kmin ? a : kmin;
         kmax = b > kmax ? b : kmax;
     }
+    // every lane now holds the same range: make it wave-uniform, so that the
+    // search below runs on the scalar unit
+    kmin = uniform_key(kmin);
+    kmax = uniform_key(kmax);
     auto count_ge = [&](Key th) -> uint32_t {
         uint32_t c = 0;
 #pragma unroll
