@@ -201,6 +201,21 @@ def test_float32_ties_decided_in_float64():
     assert tied >= n_v, tied
 
 
+def test_longest_rows_of_the_matrix_core_select():
+    """n_v = 1,280 video tiles, the most the matrix-core select kernel takes
+    (20 keys per lane in its top-k, 82 KiB of float32 score rows, one
+    workgroup per CU): every selection row exactly and the coarse branch."""
+    h, s_t, s_v, s_a = 2, 64, 64 * 1280, 64
+    announce(f"n_v = 1280: h={h} k={bsv.vsa_topk_count(s_v, 0.2)}")
+    x = synth.vsa_inputs(24, h, s_t, s_v, s_a, threads=THREADS)
+    xd = G.inputs_to_dev(x)
+    out, sel, ws = G.run_forward(xd, s_t, s_v, s_a, 0.2)
+    ref = oracle.select_coarse(x["q"], x["k"], x["v"], s_t, s_v, s_a, 0.2, threads=THREADS)
+    G.check_selection(sel.cpu().numpy(), ref, exempt_ok=False)
+    w = G.read_workspace(ws, h, s_t, s_v, s_a)
+    np.testing.assert_allclose(w["coarse"], ref["coarse"], rtol=2e-5, atol=2e-7)
+
+
 @pytest.mark.slow
 def test_long_rows_use_the_radix_select():
     """n_v = 1,300 video tiles: rows too long for the register bisection go
