@@ -107,13 +107,14 @@ size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_le
  *              the total lie the partial results of text/audio query tiles
  *              whose key list the fine stage splits into parts (float32,
  *              33,280 bytes per part, up to 4 parts per tile; none without
- *              video tiles) and, in the last 1 KiB, the fine stage's
- *              work-queue counters, which every call clears before use
+ *              video tiles) and, in the last 1,280 bytes, the fine
+ *              stage's ten work-queue counters, which every call clears
+ *              before use
  * Returns VSA_OK or a shape error.  Host only. */
 vsa_status vsa_workspace_layout(int32_t num_heads, int64_t text_len, int64_t video_len,
                                 int64_t audio_len, size_t offsets[7]);
 
-/* The whole forward pass: pooling and V packing, ranking + exact top-k +
+/* The whole forward pass: pooling and K/V packing, ranking + exact top-k +
  * coarse branch, then fine block-sparse attention with the gated
  * combination.  Writes out [S][H][128] bf16 and selected_tiles
  * [H][n_v][k].  gate and selected_tiles may be NULL only when video_len is
