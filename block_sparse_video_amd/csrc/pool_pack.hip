@@ -282,8 +282,16 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t* __restrict
         double s = 0.0;
         for (int r = 0; r < n; ++r) s += (double)__uint_as_float((uint32_t)tl[r * kPitch + d] << 16);
         const float mean = (float)(s / (double)n);
-        if (tid < kD) kbar_t[((int64_t)h * kD + d) * n_v + u] = mean;
-        else vbar[((int64_t)h * n_v + u) * kD + d] = mean;
+        if (tid < kD) {
+            kbar_t[((int64_t)h * kD + d) * n_v + u] = mean;
+        } else {
+            // transposed, rows padded to vbar_pitch(n_v); the last tile zeroes the padding
+            const int ldv = vbar_pitch(n_v);
+            float* vrow = vbar + ((int64_t)h * kD + d) * ldv;
+            vrow[u] = mean;
+            if (u == n_v - 1)
+                for (int w = n_v; w < ldv; ++w) vrow[w] = 0.0f;
+        }
     }
     const int64_t base = ((int64_t)h * N + t) * (kT * kD);
 #pragma unroll

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __rest
     double acc[RH];
 #pragma unroll
     for (int i = 0; i < RH; ++i) acc[i] = 0.0;
-    const float* vb = vbar + (int64_t)h * n_v * kD + d;
+    const float* vb = vbar + ((int64_t)h * kD + d) * vbar_pitch(n_v);  // transposed pooled V
     const double* prow[RH];
 #pragma unroll
     for (int i = 0; i < RH; ++i) prow[i] = sc + min(half * RH + i, R - 1) * ldw;
@@ -187,12 +187,11 @@ __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __rest
     float vn[32];
     auto load_group = [&](int w0) {
         if (w0 + 32 <= n_v) {
-            const float* p = vb + (int64_t)w0 * kD;
 #pragma unroll
-            for (int i = 0; i < 32; ++i) vn[i] = p[i * kD];
+            for (int i = 0; i < 32; ++i) vn[i] = vb[w0 + i];
         } else {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) vn[i] = vb[(int64_t)min(w0 + i, n_v - 1) * kD];
+            for (int i = 0; i < 32; ++i) vn[i] = vb[min(w0 + i, n_v - 1)];
         }
     };
     load_group(0);
@@ -246,9 +245,10 @@ constexpr int kRowsM = 16;   // query rows per workgroup: the instruction's M
 constexpr int kWavesM = 8;   // 512 threads
 constexpr int kSlotsM = 20;  // keys per lane in the top-k (n_v <= 64 * 20)
 
-// LDS row pitch in floats: at least n_v, 8 modulo 64, so that the 16 rows of
-// one operand read fall on 8 different groups of banks.
-__host__ __device__ inline int mfma_pitch(int n_v) { return ((n_v + 55) / 64) * 64 + 8; }
+// LDS row pitch in floats: at least n_v rounded up to 16 (whole 16-key
+// blocks), 8 modulo 64, so that the 16 rows of one operand read fall on 8
+// different groups of banks.
+__host__ __device__ inline int mfma_pitch(int n_v) { return ((((n_v + 15) & ~15) + 55) / 64) * 64 + 8; }
 
 __device__ __forceinline__ f64x4 mfma64(double a, double b, f64x4 c) {
     return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
@@ -453,40 +453,30 @@ __global__ __launch_bounds__(512, 4) void select_coarse_mfma_kernel(
     __syncthreads();
 
     // ---- coarse C[r][d] = sum_w P[r][w] Vbar[w][d] / sum_w P[r][w] --------
-    // wave wv: dims 16 wv .. 16 wv + 15; even and odd key groups accumulate in
-    // two chains, added at the end.  Rows past n_v (ragged last workgroup)
-    // compute garbage that is never stored.
+    // wave wv: dims 16 wv .. 16 wv + 15, one 16-key block per step: MFMA t of
+    // block j takes key 16 j + 4 (lane / 16) + t in lane group lane / 16, so a
+    // lane reads its four weights (one LDS read) and its four pooled V values
+    // (one load from the transposed, padded rows) at once; padding keys have
+    // weight 0 and value 0.  Even and odd t accumulate in two chains, added
+    // at the end.  Rows past n_v (ragged last workgroup) compute garbage that
+    // is never stored.
     {
-        const float* vb = vbar + (int64_t)h * n_v * kD + 16 * wv + lr;
-        const float* prow = sc + lr * pitch + lk;
-        const int nks = (n_v + 3) / 4;
+        const float* vb = vbar + ((int64_t)h * kD + 16 * wv + lr) * vbar_pitch(n_v) + 4 * lk;
+        const float* prow = sc + lr * pitch + 4 * lk;
+        const int nb16 = (n_v + 15) / 16;
         f64x4 c0 = {0.0, 0.0, 0.0, 0.0}, c1 = c0;
-        constexpr int G = 16;  // key groups per batch; the next batch is requested
-                               // while the current one is multiplied
-        float vv[G], vn[G];
-        double pa[G], pn[G];
-        auto load_batch = [&](int ks0, float (&v)[G], double (&pw)[G]) {
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                const int ks = min(ks0 + i, nks - 1);
-                v[i] = vb[(int64_t)min(4 * ks + lk, n_v - 1) * kD];
-                pw[i] = ks0 + i < nks ? (double)prow[4 * ks] : 0.0;
+        float4 pn = *(const float4*)prow, vn = *(const float4*)vb;
+#pragma unroll 2
+        for (int j = 0; j < nb16; ++j) {
+            const float4 pw = pn, vv = vn;
+            if (j + 1 < nb16) {
+                pn = *(const float4*)(prow + 16 * (j + 1));
+                vn = *(const float4*)(vb + 16 * (j + 1));
             }
-        };
-        load_batch(0, vn, pn);
-#pragma unroll 1
-        for (int ks0 = 0; ks0 < nks; ks0 += G) {
-#pragma unroll
-            for (int i = 0; i < G; ++i) {
-                vv[i] = vn[i];
-                pa[i] = pn[i];
-            }
-            if (ks0 + G < nks) load_batch(ks0 + G, vn, pn);
-#pragma unroll
-            for (int i = 0; i < G; i += 2) {
-                c0 = mfma64(pa[i], (double)vv[i], c0);
-                c1 = mfma64(pa[i + 1], (double)vv[i + 1], c1);
-            }
+            c0 = mfma64((double)pw.x, (double)vv.x, c0);
+            c1 = mfma64((double)pw.y, (double)vv.y, c1);
+            c0 = mfma64((double)pw.z, (double)vv.z, c0);
+            c1 = mfma64((double)pw.w, (double)vv.w, c1);
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {

@@ -49,7 +49,7 @@ struct Prep {
 struct Layout {
     size_t qbar64;  // double [H][n_v][128]
     size_t kbar_t;  // float  [H][128][n_v]
-    size_t vbar;    // float  [H][n_v][128]
+    size_t vbar;    // float  [H][128][vbar_pitch(n_v)] (transposed; columns past n_v are zero)
     size_t coarse;  // float  [H][n_v][128]
     size_t kpack;   // bf16   [H][N][2][8][64][8]      K tiles in MFMA A-operand order
     size_t vpack;   // bf16   [H][N][2][4][2][64][8]   V^T tiles in MFMA A-operand order
@@ -77,6 +77,10 @@ constexpr size_t kSchedBytes = (kQueues + 2) * 128;
 constexpr int kMaxParts = 4;
 constexpr size_t kPartBytes = (64 * 128 + 128) * sizeof(float);
 
+// Row pitch (floats) of the transposed pooled V: n_v rounded up to 16, so
+// that every 16-key block of a row is 64-byte aligned and lies inside it.
+__host__ __device__ inline int vbar_pitch(int n_v) { return (n_v + 15) & ~15; }
+
 // pooled = false: no pooled statistics or coarse regions (a caller that only
 // packs tiles and routes with the SubBlock piece means).
 inline Layout make_layout(const Shape& s, bool subblock = false, bool pooled = true) {
@@ -85,7 +89,7 @@ inline Layout make_layout(const Shape& s, bool subblock = false, bool pooled = t
     const size_t hv = pooled ? (size_t)s.H * (size_t)s.n_v * kD : 0;
     L.qbar64 = off; off = align_up(off + hv * sizeof(double));
     L.kbar_t = off; off = align_up(off + hv * sizeof(float));
-    L.vbar = off;   off = align_up(off + hv * sizeof(float));
+    L.vbar = off;   off = align_up(off + (pooled ? (size_t)s.H * kD * vbar_pitch(s.n_v) : 0) * sizeof(float));
     L.coarse = off; off = align_up(off + hv * sizeof(float));
     L.kpack = off;  off = align_up(off + (size_t)s.H * (size_t)s.N * kT * kD * 2);
     L.vpack = off;  off = align_up(off + (size_t)s.H * (size_t)s.N * kT * kD * 2);

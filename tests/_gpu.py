@@ -105,7 +105,8 @@ def read_workspace(ws: torch.Tensor, h, s_t, s_v, s_a) -> dict:
 
     return {"qbar64": view(lay["qbar64"], np.float64, (h, n_v, D)),
             "kbar_t": view(lay["kbar_t"], np.float32, (h, D, n_v)),
-            "vbar": view(lay["vbar"], np.float32, (h, n_v, D)),
+            "vbar": view(lay["vbar"], np.float32, (h, D, (n_v + 15) // 16 * 16))[:, :, :n_v]
+                    .transpose(0, 2, 1),
             "coarse": view(lay["coarse"], np.float32, (h, n_v, D))}
 
 
