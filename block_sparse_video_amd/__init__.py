@@ -92,7 +92,7 @@ def vsa_workspace_layout(num_heads: int, text_len: int, video_len: int, audio_le
     off = (ctypes.c_size_t * 7)()
     _check(load().vsa_workspace_layout(num_heads, text_len, video_len, audio_len, off),
            "vsa_workspace_layout")
-    names = ("qbar64", "kbar_t", "vbar", "coarse", "kpack", "vpack", "total")
+    names = ("qbar64", "kbar", "vbar", "coarse", "kpack", "vpack", "total")
     return {n: int(off[i]) for i, n in enumerate(names)}
 
 

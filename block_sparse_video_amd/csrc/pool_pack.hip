@@ -50,9 +50,9 @@ __global__ __launch_bounds__(128) void pool_q_kernel(const uint16_t* __restrict_
         acc[6] += (double)bf16_lo(w.w);
         acc[7] += (double)bf16_hi(w.w);
     }
-    double* o = qbar64 + ((int64_t)h * n_v + u) * kD + c * 8;
+    double* o = qbar64 + ((int64_t)h * n_v + u) * kD;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = (double)(float)(acc[e] / (double)n);
+    for (int e = 0; e < 8; ++e) o[pooled_dim_pos(c * 8 + e)] = (double)(float)(acc[e] / (double)n);
 }
 
 // ---- attention preprocessing: learned RMSNorm and partial 3D RoPE ---------
@@ -180,9 +180,9 @@ __global__ __launch_bounds__(128) void prep_q_kernel(const uint16_t* __restrict_
         }
     }
     if (video && active) {
-        double* o = qbar64 + ((int64_t)h * n_v + (j - n_t)) * kD + c * 8;
+        double* o = qbar64 + ((int64_t)h * n_v + (j - n_t)) * kD;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = (double)(float)(acc[e] / (double)n);
+        for (int e = 0; e < 8; ++e) o[pooled_dim_pos(c * 8 + e)] = (double)(float)(acc[e] / (double)n);
     }
 }
 
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t* __restrict
                                                       int ldh, int n_t, int n_v, int N, int64_t S_t,
                                                       int64_t S_v, int64_t V_t, int64_t V_v,
                                                       int64_t V_a, PrepArgs pa, int pool,
-                                                      float* __restrict__ kbar_t,
+                                                      float* __restrict__ kbar,
                                                       float* __restrict__ vbar,
                                                       uint16_t* __restrict__ kpack,
                                                       uint16_t* __restrict__ vpack) {
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void pack_kv_kernel(const uint16_t* __restrict
         for (int r = 0; r < n; ++r) s += (double)__uint_as_float((uint32_t)tl[r * kPitch + d] << 16);
         const float mean = (float)(s / (double)n);
         if (tid < kD) {
-            kbar_t[((int64_t)h * kD + d) * n_v + u] = mean;
+            kbar[((int64_t)h * n_v + u) * kD + pooled_dim_pos(d)] = mean;
         } else {
             // transposed, rows padded to vbar_pitch(n_v); the last tile zeroes the padding
             const int ldv = vbar_pitch(n_v);
@@ -340,7 +340,7 @@ hipError_t launch_pool_pack(const uint16_t* q, const uint16_t* k, const uint16_t
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(pack_kv_kernel, dim3(s.N, s.H), dim3(256), 0, stream, k, v, s.H, s.ldh, s.n_t, s.n_v,
-                       s.N, s.S_t, s.S_v, s.V_t, s.V_v, s.V_a, ka, pooled ? 1 : 0, (float*)(ws + L.kbar_t),
+                       s.N, s.S_t, s.S_v, s.V_t, s.V_v, s.V_a, ka, pooled ? 1 : 0, (float*)(ws + L.kbar),
                        (float*)(ws + L.vbar), (uint16_t*)(ws + L.kpack), (uint16_t*)(ws + L.vpack));
     return hipGetLastError();
 }

@@ -31,7 +31,7 @@ namespace {
 
 template <int R, int NS>
 __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __restrict__ qbar64,
-                                                            const float* __restrict__ kbar_t,
+                                                            const float* __restrict__ kbar,
                                                             const float* __restrict__ vbar, int n_v,
                                                             int k, int ldw, float alpha,
                                                             int32_t* __restrict__ sel,
@@ -52,18 +52,20 @@ __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __rest
         const double* qb[R];
 #pragma unroll
         for (int r = 0; r < R; ++r) qb[r] = qbar64 + ((int64_t)h * n_v + min(u0 + r, n_v - 1)) * kD;
-        const float* kb = kbar_t + (int64_t)h * kD * n_v;
+        const float* kb = kbar + (int64_t)h * n_v * kD;
         for (int w0 = 0; w0 < n_v; w0 += 256) {
             const int w = w0 + tid;
             const int wc = min(w, n_v - 1);
+            const float* kw = kb + (int64_t)wc * kD;
             double acc[R];
 #pragma unroll
             for (int r = 0; r < R; ++r) acc[r] = 0.0;
 #pragma unroll 8
             for (int d = 0; d < kD; ++d) {
-                const double kd = (double)kb[(int64_t)d * n_v + wc];
+                const int pd = pooled_dim_pos(d);
+                const double kd = (double)kw[pd];
 #pragma unroll
-                for (int r = 0; r < R; ++r) acc[r] = __fma_rn(qb[r][d], kd, acc[r]);
+                for (int r = 0; r < R; ++r) acc[r] = __fma_rn(qb[r][pd], kd, acc[r]);
             }
             if (w < n_v) {
 #pragma unroll
@@ -327,7 +329,10 @@ __device__ __forceinline__ void emit_band_resolved(const float* row, const doubl
         kb64[i] = 0ull;
         if (w < n_v && order_key32(row[w]) == t32) {
             double s = 0.0;
-            for (int d = 0; d < kD; ++d) s = __builtin_fma(qrow[d], (double)kb_h[(int64_t)d * n_v + w], s);
+            for (int d = 0; d < kD; ++d) {
+                const int pd = pooled_dim_pos(d);
+                s = __builtin_fma(qrow[pd], (double)kb_h[(int64_t)w * kD + pd], s);
+            }
             kb64[i] = order_key(s + 0.0);
         }
     }
@@ -354,7 +359,7 @@ __device__ __forceinline__ void emit_band_resolved(const float* row, const doubl
 }
 
 __global__ __launch_bounds__(512, 4) void select_coarse_mfma_kernel(
-    const double* __restrict__ qbar64, const float* __restrict__ kbar_t,
+    const double* __restrict__ qbar64, const float* __restrict__ kbar,
     const float* __restrict__ vbar, int n_v, int k, int pitch, float alpha,
     int32_t* __restrict__ sel, float* __restrict__ coarse) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -366,25 +371,37 @@ __global__ __launch_bounds__(512, 4) void select_coarse_mfma_kernel(
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
     const int lr = lane & 15, lk = lane >> 4;
-    const float* kb_h = kbar_t + (int64_t)h * kD * n_v;
+    const float* kb_h = kbar + (int64_t)h * n_v * kD;
 
     // ---- scores S[r][w] = sum_d Qbar[u0 + r][d] Kbar[w][d] -----------------
     // wave wv computes the 16-key blocks wv, wv + 8, ...; the A operands (this
     // workgroup's query rows, all 32 dimension groups) are loaded once, and
-    // each block is one chain of 32 MFMAs, in d order.
+    // each block is one chain of 32 MFMAs, in d order.  Lane group lk feeds
+    // dims 4 ds + lk, stored contiguously (pooled_dim_pos), so a lane's 32
+    // operands of a row are one 256-byte (Q) or 128-byte (K) run.
     {
         double qa[32];
-        const double* qrow = qbar64 + ((int64_t)h * n_v + min(u0 + lr, n_v - 1)) * kD + lk;
+        const double* qrow = qbar64 + ((int64_t)h * n_v + min(u0 + lr, n_v - 1)) * kD + 32 * lk;
 #pragma unroll
-        for (int ds = 0; ds < 32; ++ds) qa[ds] = qrow[4 * ds];
-        const float* kb = kb_h + (int64_t)lk * n_v;
+        for (int ds = 0; ds < 32; ds += 2) {
+            const double2 q2 = *(const double2*)(qrow + ds);
+            qa[ds] = q2.x;
+            qa[ds + 1] = q2.y;
+        }
         const int nblk = (n_v + 15) / 16;
 #pragma unroll 1
         for (int b = wv; b < nblk; b += kWavesM) {
             const int w = min(16 * b + lr, n_v - 1);
+            const float* kw = kb_h + (int64_t)w * kD + 32 * lk;
             float kc[32];
 #pragma unroll
-            for (int ds = 0; ds < 32; ++ds) kc[ds] = kb[(int64_t)4 * ds * n_v + w];
+            for (int ds = 0; ds < 32; ds += 4) {
+                const float4 k4 = *(const float4*)(kw + ds);
+                kc[ds] = k4.x;
+                kc[ds + 1] = k4.y;
+                kc[ds + 2] = k4.z;
+                kc[ds + 3] = k4.w;
+            }
             f64x4 acc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
             for (int ds = 0; ds < 32; ++ds) acc = mfma64(qa[ds], (double)kc[ds], acc);
@@ -498,7 +515,7 @@ hipError_t launch_r(const Shape& s, int32_t* sel, uint8_t* ws, const Layout& L, 
     dim3 grid((s.n_v + R - 1) / R, s.H);
     const float alpha = (float)(1.0 / 11.313708498984761);  // 1/sqrt(128)
     hipLaunchKernelGGL((select_coarse_kernel<R, NS>), grid, dim3(256), lds, stream,
-                       (const double*)(ws + L.qbar64), (const float*)(ws + L.kbar_t),
+                       (const double*)(ws + L.qbar64), (const float*)(ws + L.kbar),
                        (const float*)(ws + L.vbar), s.n_v, s.k, ldw, alpha, sel,
                        (float*)(ws + L.coarse));
     return hipGetLastError();
@@ -525,7 +542,7 @@ hipError_t launch_select_coarse(const Shape& s, int32_t* sel, uint8_t* ws, const
         dim3 grid((s.n_v + kRowsM - 1) / kRowsM, s.H);
         const float alpha = (float)(1.0 / 11.313708498984761);  // 1/sqrt(128)
         hipLaunchKernelGGL(select_coarse_mfma_kernel, grid, dim3(64 * kWavesM), lds, stream,
-                           (const double*)(ws + L.qbar64), (const float*)(ws + L.kbar_t),
+                           (const double*)(ws + L.qbar64), (const float*)(ws + L.kbar),
                            (const float*)(ws + L.vbar), s.n_v, s.k, mfma_pitch(s.n_v), alpha, sel,
                            (float*)(ws + L.coarse));
         return hipGetLastError();

@@ -193,7 +193,7 @@ vsa_status vsa_workspace_layout(int32_t num_heads, int64_t text_len, int64_t vid
     if (st != VSA_OK) return st;
     const Layout L = vsa::make_layout(s);
     offsets[0] = L.qbar64;
-    offsets[1] = L.kbar_t;
+    offsets[1] = L.kbar;
     offsets[2] = L.vbar;
     offsets[3] = L.coarse;
     offsets[4] = L.kpack;

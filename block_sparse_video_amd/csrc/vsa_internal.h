@@ -47,8 +47,8 @@ struct Prep {
 
 // Workspace regions (byte offsets from the workspace base).
 struct Layout {
-    size_t qbar64;  // double [H][n_v][128]
-    size_t kbar_t;  // float  [H][128][n_v]
+    size_t qbar64;  // double [H][n_v][128], dims in pooled_dim_pos order
+    size_t kbar;    // float  [H][n_v][128], dims in pooled_dim_pos order
     size_t vbar;    // float  [H][128][vbar_pitch(n_v)] (transposed; columns past n_v are zero)
     size_t coarse;  // float  [H][n_v][128]
     size_t kpack;   // bf16   [H][N][2][8][64][8]      K tiles in MFMA A-operand order
@@ -77,6 +77,11 @@ constexpr size_t kSchedBytes = (kQueues + 2) * 128;
 constexpr int kMaxParts = 4;
 constexpr size_t kPartBytes = (64 * 128 + 128) * sizeof(float);
 
+// Storage order of the 128 dims of a pooled Q or K row: dim d = 4 s + g sits
+// at position 32 g + s, so that the float64 MFMA's lane group g (which feeds
+// dims 4 s + g of the d-order chain, s = 0..31) reads 32 consecutive values.
+__host__ __device__ inline int pooled_dim_pos(int d) { return (d & 3) * 32 + (d >> 2); }
+
 // Row pitch (floats) of the transposed pooled V: n_v rounded up to 16, so
 // that every 16-key block of a row is 64-byte aligned and lies inside it.
 __host__ __device__ inline int vbar_pitch(int n_v) { return (n_v + 15) & ~15; }
@@ -88,7 +93,7 @@ inline Layout make_layout(const Shape& s, bool subblock = false, bool pooled = t
     size_t off = 0;
     const size_t hv = pooled ? (size_t)s.H * (size_t)s.n_v * kD : 0;
     L.qbar64 = off; off = align_up(off + hv * sizeof(double));
-    L.kbar_t = off; off = align_up(off + hv * sizeof(float));
+    L.kbar = off;   off = align_up(off + hv * sizeof(float));
     L.vbar = off;   off = align_up(off + (pooled ? (size_t)s.H * kD * vbar_pitch(s.n_v) : 0) * sizeof(float));
     L.coarse = off; off = align_up(off + hv * sizeof(float));
     L.kpack = off;  off = align_up(off + (size_t)s.H * (size_t)s.N * kT * kD * 2);

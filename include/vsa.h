@@ -98,7 +98,8 @@ size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_le
 
 /* Byte offsets of the workspace regions, for inspection by tests:
  *   offsets[0] pooled Q   float64 [H][n_v][128] (the FP32 statistic, widened)
- *   offsets[1] pooled K   float32 [H][128][n_v] (transposed)
+ *   offsets[1] pooled K   float32 [H][n_v][128]
+ *              (in both, dim d = 4 s + g of a row is stored at 32 g + s)
  *   offsets[2] pooled V   float32 [H][128][n_v rounded up to 16] (transposed;
  *              the columns past n_v are zero)
  *   offsets[3] coarse     float32 [H][n_v][128]

@@ -103,8 +103,10 @@ def read_workspace(ws: torch.Tensor, h, s_t, s_v, s_a) -> dict:
         n = int(np.prod(shape)) * np.dtype(dtype).itemsize
         return raw[off:off + n].view(dtype).reshape(shape)
 
-    return {"qbar64": view(lay["qbar64"], np.float64, (h, n_v, D)),
-            "kbar_t": view(lay["kbar_t"], np.float32, (h, D, n_v)),
+    # pooled Q and K rows store dim d = 4 s + g at position 32 g + s
+    pos = np.array([(d & 3) * 32 + (d >> 2) for d in range(D)])
+    return {"qbar64": view(lay["qbar64"], np.float64, (h, n_v, D))[:, :, pos],
+            "kbar": view(lay["kbar"], np.float32, (h, n_v, D))[:, :, pos],
             "vbar": view(lay["vbar"], np.float32, (h, D, (n_v + 15) // 16 * 16))[:, :, :n_v]
                     .transpose(0, 2, 1),
             "coarse": view(lay["coarse"], np.float32, (h, n_v, D))}

@@ -57,7 +57,7 @@ def test_workspace_bytes_and_layout():
     lay = bsv.vsa_workspace_layout(56, 1024, 72576, 1024)
     assert lay["total"] == n
     h, n_v, N = 56, 1134, 1166
-    assert lay["kbar_t"] - lay["qbar64"] >= h * n_v * 128 * 8
+    assert lay["kbar"] - lay["qbar64"] >= h * n_v * 128 * 8
     assert lay["total"] - lay["vpack"] >= h * N * 64 * 128 * 2
     assert lay["vpack"] - lay["kpack"] >= h * N * 64 * 128 * 2
     assert all(v % 256 == 0 for v in lay.values())
