@@ -40,6 +40,7 @@ FLOP_PER_PAIR = 4 * TILE * TILE * D          # QK^T + PV of one 64x64 tile pair
 PEAK_BF16_TFLOPS = 2500.0                   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E (published)
 PEAK_FP64_TFLOPS = 78.6                     # MI355X dense fp64 MFMA (published)
+PEAK_FP32_MFMA_TFLOPS = 157.3               # MI355X dense fp32 MFMA (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fine_attn_traffic_10s_56h.txt")
 FINE_SOURCE = os.path.join(ROOT, "block_sparse_video_amd", "csrc", "fine_attn.hip")
 
@@ -60,9 +61,10 @@ def pool_pack_bytes(h, s_t, s_v, s_a):
 
 
 def select_coarse_work(h, s_v, k):
-    """Algorithmic work of stage 2: float64 tile scores (2 n_v^2 128 FLOP per
-    head) and the coarse product (the same count), and its HBM bytes (pooled
-    statistics in, selection and coarse vectors out)."""
+    """Algorithmic work of stage 2: tile scores (2 n_v^2 128 FLOP per head)
+    and the coarse product (the same count), both on the float32 matrix
+    instruction, and its HBM bytes (pooled statistics in, selection and
+    coarse vectors out)."""
     n_v = s_v // TILE
     flop = 2 * 2.0 * h * n_v * n_v * D
     nbytes = h * n_v * D * (8 + 4 + 4) + h * n_v * k * 4 + h * n_v * D * 4
@@ -453,8 +455,8 @@ def main():
             "pool_pack_ms": r["stage_ms"][0],
             "pool_pack_GBs": pool_pack_bytes(h, s_t, s_v, s_a) / (r["stage_ms"][0] * 1e-3) / 1e9,
             "select_coarse_ms": r["stage_ms"][1],
-            "select_coarse_fp64_tflops": select_coarse_work(h, s_v, kk)[0] / (r["stage_ms"][1] * 1e-3) / 1e12,
-            "select_coarse_fp64_frac_of_78.6": select_coarse_work(h, s_v, kk)[0] / (r["stage_ms"][1] * 1e-3) / 1e12 / PEAK_FP64_TFLOPS,
+            "select_coarse_tflops": select_coarse_work(h, s_v, kk)[0] / (r["stage_ms"][1] * 1e-3) / 1e12,
+            "select_coarse_frac_of_fp32_mfma_157.3": select_coarse_work(h, s_v, kk)[0] / (r["stage_ms"][1] * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS,
             "select_coarse_GBs": select_coarse_work(h, s_v, kk)[1] / (r["stage_ms"][1] * 1e-3) / 1e9,
             "fine_attn_ms": fine_ms,
             "forward_entry_ms": r["forward_ms"],

@@ -222,26 +222,33 @@ __global__ __launch_bounds__(256) void select_coarse_kernel(const double* __rest
 
 // ---- matrix-core version: 16 query rows per workgroup ----------------------
 //
-// Both products of this stage run on the float64 matrix instruction
-// v_mfma_f64_16x16x4f64, which on gfx950 adds its four products to the
-// accumulator one after another, each rounded: a chain of them over the
-// dimension groups d = 0..3, 4..7, ... is bit for bit the float64
-// multiply-add chain in d order, i.e. the scores above.  (Measured on the
-// device against every other summation order: 512,000 of 512,000 results
-// agree with the sequential chain, about 70% with the others.)
+// Both products run on the float32 matrix instruction v_mfma_f32_16x16x4f32
+// (twice the float64 one's rate on gfx950).  Each score is eight chains of
+// four instructions (16 products of dims 16c .. 16c + 15, from a zero
+// accumulator), whose float32 results are added in float64 and rounded once
+// to float32.  The stored score a differs from the exact float64 score e by
+//   |a - e| <= eps = 2.1e-6 * |Qbar[u]| * max_w |Kbar[w]|  (+ a denormal term)
+// (Euclidean norms): a 16-term float32 dot product of any summation order
+// and any rounding mode is within gamma_16 = 16u / (1 - 16u), u = 2^-23, of
+// the sum of |products|, which Cauchy-Schwarz bounds by the norms; the
+// float64 sum adds ~1e-15 and the final rounding 2^-24 of that bound.
+// Selection stays exact: with T the k-th largest stored score of a row,
+// every key above T + 2 eps is in the exact top k and every key below
+// T - 2 eps is not (at least k keys have e >= T - eps, at most k - 1 have
+// e > T + eps), so only the band [T - 2 eps, T + 2 eps] can need more.  When
+// the band holds more keys than are still to be taken, their float64 scores
+// are recomputed (the d-order chain of exact products, the oracle's
+// definition) and ranked among themselves, ties to the lower index.  The
+// band is ~1e-4 of the score spread: almost every row takes it whole.
+// The coarse product runs on the same float32 instruction, in chains of four
+// (16 keys) whose results are added in float64.
 // Operand layout (lane l): A[row l % 16][k l / 16], B[k l / 16][col l % 16];
-// result D[row l / 16 + 4 v][col l % 16] in element v.
+// result D[row 4 (l / 16) + v][col l % 16] in element v.
 //
 // The 16 score rows are kept in LDS as float32 (74 KiB at 1,134 tiles, so two
 // workgroups share a CU and one's top-k overlaps the other's matrix work).
-// Rounding to float32 is monotone, so a float32 score above the row's k-th
-// largest float32 value belongs to a float64 score above every float64 score
-// at or below it: the selection is exact except inside the band of scores
-// whose float32 value equals the k-th.  When that band holds more entries
-// than are still to be taken, their float64 scores are recomputed (the same
-// d-order chain, with the same exact products) and ranked among themselves,
-// ties to the lower index.
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowsM = 16;   // query rows per workgroup: the instruction's M
 constexpr int kWavesM = 8;   // 512 threads
@@ -252,14 +259,36 @@ constexpr int kSlotsM = 20;  // keys per lane in the top-k (n_v <= 64 * 20)
 // different groups of banks.
 __host__ __device__ inline int mfma_pitch(int n_v) { return ((((n_v + 15) & ~15) + 55) / 64) * 64 + 8; }
 
-__device__ __forceinline__ f64x4 mfma64(double a, double b, f64x4 c) {
-    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Bound on |stored score - float64 score| per unit of |Qbar[u]| max|Kbar[w]|:
+// gamma_16 (u = 2^-23) + 2^-24 + the float64 sum, ~1.967e-6, with ~7% to
+// spare (which also covers the float32 sum of squares behind max|Kbar[w]|).
+constexpr double kScoreErr = 2.1e-6;
+// Flushed denormal operands or partial results: at most 2^-126 per product
+// or addition, times the larger operand; 256 of them per score.
+constexpr double kScoreDenorm = 0x1p-117;
+
 // Order-preserving map of a float32 to uint32 (key 0 is never a finite score).
+// Consecutive keys are consecutive floats (-0 and +0 apart), so key + 1 is
+// the next float up.
 __device__ __forceinline__ uint32_t order_key32(float x) {
     const uint32_t b = __float_as_uint(x);
     return (b >> 31) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key32_value(uint32_t key) {
+    return __uint_as_float((key >> 31) ? (key & 0x7FFFFFFFu) : ~key);
+}
+// Smallest key whose float is >= x, and largest whose float is <= x.
+__device__ __forceinline__ uint32_t key32_at_or_above(double x) {
+    const float f = (float)x + 0.0f;
+    return order_key32(f) + ((double)f < x ? 1u : 0u);
+}
+__device__ __forceinline__ uint32_t key32_at_or_below(double x) {
+    const float f = (float)x + 0.0f;
+    return order_key32(f) - ((double)f > x ? 1u : 0u);
 }
 
 __device__ __forceinline__ uint32_t uniform_key(uint32_t x) {
@@ -312,28 +341,31 @@ __device__ __forceinline__ Key kth_largest(const Key (&kv)[NS], uint32_t kk, uin
     return lo;
 }
 
-// Selection of one row whose band (float32 score equal to the k-th largest,
-// t32) holds more entries than the `need` still to take: the band's float64
-// scores are recomputed as the d-order chain of exact products (the value the
-// matrix instruction produced), and the row's selection is every key above
-// t32 plus the band's `need` best by (float64 score desc, index asc), written
-// in ascending index order.  Rows whose band is exactly what is needed
-// (nearly all) never run it.
+// Selection of one row whose band (stored scores with keys in [lo, hi])
+// holds more entries than the `need` still to take: the band's float64
+// scores are recomputed as the d-order chain of exact products (the oracle's
+// scores), and the row's selection is every key above hi plus the band's
+// `need` best by (float64 score desc, index asc), written in ascending index
+// order.  Rows whose band is exactly what is needed (nearly all) never run it.
 __device__ __forceinline__ void emit_band_resolved(const float* row, const double* qrow,
-                                                const float* kb_h, int n_v, int k, uint32_t t32,
-                                                uint32_t need, int lane, int32_t* out) {
+                                                const float* kb_h, int n_v, int k, uint32_t lo,
+                                                uint32_t hi, uint32_t need, int lane,
+                                                int32_t* out) {
     uint64_t kb64[kSlotsM];
 #pragma unroll
     for (int i = 0; i < kSlotsM; ++i) {
         const int w = lane + 64 * i;
         kb64[i] = 0ull;
-        if (w < n_v && order_key32(row[w]) == t32) {
-            double s = 0.0;
-            for (int d = 0; d < kD; ++d) {
-                const int pd = pooled_dim_pos(d);
-                s = __builtin_fma(qrow[pd], (double)kb_h[(int64_t)w * kD + pd], s);
+        if (w < n_v) {
+            const uint32_t key = order_key32(row[w]);
+            if (key >= lo && key <= hi) {
+                double s = 0.0;
+                for (int d = 0; d < kD; ++d) {
+                    const int pd = pooled_dim_pos(d);
+                    s = __builtin_fma(qrow[pd], (double)kb_h[(int64_t)w * kD + pd], s);
+                }
+                kb64[i] = order_key(s + 0.0);
             }
-            kb64[i] = order_key(s + 0.0);
         }
     }
     uint32_t gt64;
@@ -349,7 +381,7 @@ __device__ __forceinline__ void emit_band_resolved(const float* row, const doubl
         const bool eq64 = kb64[i] != 0ull && kb64[i] == t64;
         const uint64_t em = __ballot(eq64);
         const uint32_t erank = eqseen + (uint32_t)__popcll(em & lt_mask);
-        const bool take = key > t32 || kb64[i] > t64 || (eq64 && erank < need64);
+        const bool take = key > hi || kb64[i] > t64 || (eq64 && erank < need64);
         const uint64_t tm = __ballot(take);
         const uint32_t pos = outc + (uint32_t)__popcll(tm & lt_mask);
         if (take && valid && pos < (uint32_t)k) out[pos] = w;
@@ -365,6 +397,8 @@ __global__ __launch_bounds__(512, 4) void select_coarse_mfma_kernel(
     extern __shared__ __align__(16) unsigned char smem[];
     float* sc = (float*)smem;                          // [16][pitch] scores, later weights
     double* rowsum = (double*)(sc + kRowsM * pitch);   // [16]
+    double* qnorm2 = rowsum + kRowsM;                  // [16] |Qbar[u0 + r]|^2
+    float* knorm2 = (float*)(qnorm2 + kRowsM);         // [8] per wave: max |Kbar[w]|^2
 
     const int h = blockIdx.y;
     const int u0 = blockIdx.x * kRowsM;
@@ -373,21 +407,32 @@ __global__ __launch_bounds__(512, 4) void select_coarse_mfma_kernel(
     const int lr = lane & 15, lk = lane >> 4;
     const float* kb_h = kbar + (int64_t)h * n_v * kD;
 
-    // ---- scores S[r][w] = sum_d Qbar[u0 + r][d] Kbar[w][d] -----------------
+    // ---- scores S[r][w] ~ sum_d Qbar[u0 + r][d] Kbar[w][d] ------------------
     // wave wv computes the 16-key blocks wv, wv + 8, ...; the A operands (this
-    // workgroup's query rows, all 32 dimension groups) are loaded once, and
-    // each block is one chain of 32 MFMAs, in d order.  Lane group lk feeds
-    // dims 4 ds + lk, stored contiguously (pooled_dim_pos), so a lane's 32
-    // operands of a row are one 256-byte (Q) or 128-byte (K) run.
+    // workgroup's query rows, all 32 dimension groups) are loaded once.  Lane
+    // group lk feeds dims 4 ds + lk, stored contiguously (pooled_dim_pos), so
+    // a lane's 32 operands of a row are one 256-byte (Q) or 128-byte (K) run.
+    // Each chain of four instructions (dims 16c .. 16c + 15) starts from zero
+    // and its result is added in float64.  The squared norms of the rows and the
+    // largest squared norm of the keys go to LDS for the selection's bound.
     {
-        double qa[32];
+        float qa[32];
         const double* qrow = qbar64 + ((int64_t)h * n_v + min(u0 + lr, n_v - 1)) * kD + 32 * lk;
+        double qq = 0.0;
 #pragma unroll
         for (int ds = 0; ds < 32; ds += 2) {
             const double2 q2 = *(const double2*)(qrow + ds);
-            qa[ds] = q2.x;
-            qa[ds + 1] = q2.y;
+            qa[ds] = (float)q2.x;  // float32 means: exact
+            qa[ds + 1] = (float)q2.y;
+            qq = __builtin_fma(q2.x, q2.x, qq);
+            qq = __builtin_fma(q2.y, q2.y, qq);
         }
+        if (wv == 0) {
+            qq += __shfl_xor(qq, 16);
+            qq += __shfl_xor(qq, 32);
+            if (lk == 0) qnorm2[lr] = qq;
+        }
+        float kmax2 = 0.0f;
         const int nblk = (n_v + 15) / 16;
 #pragma unroll 1
         for (int b = wv; b < nblk; b += kWavesM) {
@@ -403,18 +448,38 @@ __global__ __launch_bounds__(512, 4) void select_coarse_mfma_kernel(
                 kc[ds + 3] = k4.w;
             }
             f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+            float kk = 0.0f;
 #pragma unroll
-            for (int ds = 0; ds < 32; ++ds) acc = mfma64(qa[ds], (double)kc[ds], acc);
-            // x + 0.0 turns -0.0 into +0.0, so equal scores have equal keys
-            if (16 * b + lr < n_v)
+            for (int ds = 0; ds < 32; ds += 4) {
+                f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) p = mfma32(qa[ds + j], kc[ds + j], p);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[v] += (double)p[v];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) kk = fmaf(kc[ds + j], kc[ds + j], kk);
+            }
+            kk += __shfl_xor(kk, 16);
+            kk += __shfl_xor(kk, 32);
+            if (16 * b + lr < n_v) {
+                kmax2 = fmaxf(kmax2, kk);
+                // x + 0.0 turns -0.0 into +0.0, so equal scores have equal keys
 #pragma unroll
                 for (int v = 0; v < 4; ++v)
-                    sc[(lk + 4 * v) * pitch + 16 * b + lr] = (float)(acc[v] + 0.0);
+                    sc[(4 * lk + v) * pitch + 16 * b + lr] = (float)(acc[v] + 0.0);
+            }
         }
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) kmax2 = fmaxf(kmax2, __shfl_xor(kmax2, off));
+        if (lane == 0) knorm2[wv] = kmax2;
     }
     __syncthreads();
 
     // ---- exact top-k and softmax weights: rows wv and wv + 8 --------------
+    float km2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kWavesM; ++i) km2 = fmaxf(km2, knorm2[i]);
+    const double kmax = sqrt((double)km2);
 #pragma unroll 1
     for (int t = 0; t < 2; ++t) {
         const int r = wv + kWavesM * t;
@@ -429,23 +494,44 @@ __global__ __launch_bounds__(512, 4) void select_coarse_mfma_kernel(
         }
         uint32_t gt32;
         const uint32_t t32 = kth_largest(kv, (uint32_t)k, gt32);
-        const uint32_t need = (uint32_t)k - gt32;  // entries still to take from the band
-        uint32_t band = 0;
+        // the band [lo, hi] around the k-th stored score that the bound on
+        // |stored - float64 score| leaves undecided; all keys when the bound
+        // is not finite or the products could leave the float32 range
+        const double qn = sqrt(qnorm2[r]);
+        uint32_t lo = 1u, hi = 0xFFFFFFFFu;
+        if (qn * kmax < 0x1p100) {
+            const double eps = kScoreErr * qn * kmax + kScoreDenorm * (qn + kmax + 1.0);
+            const double tv = (double)key32_value(t32);
+            lo = key32_at_or_below(tv - 2.0 * eps);
+            hi = key32_at_or_above(tv + 2.0 * eps);
+        }
+        uint32_t above = 0, band = 0;
 #pragma unroll
-        for (int i = 0; i < kSlotsM; ++i) band += (uint32_t)__popcll(__ballot(kv[i] == t32));
+        for (int i = 0; i < kSlotsM; ++i) {
+            above += (uint32_t)__popcll(__ballot(kv[i] > hi));
+            band += (uint32_t)__popcll(__ballot(kv[i] >= lo && kv[i] <= hi));
+        }
+        uint32_t need = (uint32_t)k - above;  // entries still to take from the band
+        if (band < need) {
+            // cannot happen while the bound holds; rank the whole row instead
+            lo = 1u;
+            hi = 0xFFFFFFFFu;
+            need = (uint32_t)k;
+            band = (uint32_t)n_v;
+        }
         int32_t* out = sel + ((int64_t)h * n_v + u) * k;
         if (band > need) {
             // band wider than what is left to take: rank it by float64 score
-            emit_band_resolved(row, qbar64 + ((int64_t)h * n_v + u) * kD, kb_h, n_v, k, t32,
+            emit_band_resolved(row, qbar64 + ((int64_t)h * n_v + u) * kD, kb_h, n_v, k, lo, hi,
                                need, lane, out);
         } else {
-            // keys above t32 and the whole band, in ascending index order
+            // keys above the band and the whole band, in ascending index order
             const uint64_t lt_mask = (1ull << lane) - 1ull;
             uint32_t outc = 0;
 #pragma unroll
             for (int i = 0; i < kSlotsM; ++i) {
                 const int w = lane + 64 * i;
-                const bool take = kv[i] >= t32;
+                const bool take = kv[i] >= lo;
                 const uint64_t tm = __ballot(take);
                 const uint32_t pos = outc + (uint32_t)__popcll(tm & lt_mask);
                 if (take && w < n_v && pos < (uint32_t)k) out[pos] = w;
@@ -474,14 +560,17 @@ __global__ __launch_bounds__(512, 4) void select_coarse_mfma_kernel(
     // block j takes key 16 j + 4 (lane / 16) + t in lane group lane / 16, so a
     // lane reads its four weights (one LDS read) and its four pooled V values
     // (one load from the transposed, padded rows) at once; padding keys have
-    // weight 0 and value 0.  Even and odd t accumulate in two chains, added
-    // at the end.  Rows past n_v (ragged last workgroup) compute garbage that
-    // is never stored.
+    // weight 0 and value 0.  Each block's four float32 instructions start
+    // from zero and their sum is added in float64, so float32 rounding acts
+    // on 16-term partial sums only (no long float32 accumulation, whose
+    // cancellation over a thousand terms would cost the coarse vector its
+    // relative accuracy).  Rows past n_v (ragged last workgroup) compute
+    // garbage that is never stored.
     {
         const float* vb = vbar + ((int64_t)h * kD + 16 * wv + lr) * vbar_pitch(n_v) + 4 * lk;
         const float* prow = sc + lr * pitch + 4 * lk;
         const int nb16 = (n_v + 15) / 16;
-        f64x4 c0 = {0.0, 0.0, 0.0, 0.0}, c1 = c0;
+        f64x4 c = {0.0, 0.0, 0.0, 0.0};
         float4 pn = *(const float4*)prow, vn = *(const float4*)vb;
 #pragma unroll 2
         for (int j = 0; j < nb16; ++j) {
@@ -490,17 +579,19 @@ __global__ __launch_bounds__(512, 4) void select_coarse_mfma_kernel(
                 pn = *(const float4*)(prow + 16 * (j + 1));
                 vn = *(const float4*)(vb + 16 * (j + 1));
             }
-            c0 = mfma64((double)pw.x, (double)vv.x, c0);
-            c1 = mfma64((double)pw.y, (double)vv.y, c1);
-            c0 = mfma64((double)pw.z, (double)vv.z, c0);
-            c1 = mfma64((double)pw.w, (double)vv.w, c1);
+            f32x4 p = {0.0f, 0.0f, 0.0f, 0.0f};
+            p = mfma32(pw.x, vv.x, p);
+            p = mfma32(pw.y, vv.y, p);
+            p = mfma32(pw.z, vv.z, p);
+            p = mfma32(pw.w, vv.w, p);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) c[v] += (double)p[v];
         }
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const int r = lk + 4 * v;
+            const int r = 4 * lk + v;
             if (u0 + r < n_v)
-                coarse[((int64_t)h * n_v + u0 + r) * kD + 16 * wv + lr] =
-                    (float)((c0[v] + c1[v]) / rowsum[r]);
+                coarse[((int64_t)h * n_v + u0 + r) * kD + 16 * wv + lr] = (float)(c[v] / rowsum[r]);
         }
     }
 }
@@ -528,7 +619,9 @@ constexpr size_t kSelectLdsMax = 160 * 1024;
 
 size_t select_lds_bytes(int R, int ldw) { return (size_t)R * ldw * 8 + 4 * 256 * 4 + (size_t)R * 8; }
 
-size_t select_mfma_lds_bytes(int n_v) { return (size_t)kRowsM * mfma_pitch(n_v) * 4 + kRowsM * 8; }
+size_t select_mfma_lds_bytes(int n_v) {
+    return (size_t)kRowsM * mfma_pitch(n_v) * 4 + 2 * kRowsM * 8 + kWavesM * 4;
+}
 
 hipError_t launch_select_coarse(const Shape& s, int32_t* sel, uint8_t* ws, const Layout& L,
                                 hipStream_t stream) {

@@ -78,8 +78,8 @@ constexpr int kMaxParts = 4;
 constexpr size_t kPartBytes = (64 * 128 + 128) * sizeof(float);
 
 // Storage order of the 128 dims of a pooled Q or K row: dim d = 4 s + g sits
-// at position 32 g + s, so that the float64 MFMA's lane group g (which feeds
-// dims 4 s + g of the d-order chain, s = 0..31) reads 32 consecutive values.
+// at position 32 g + s, so that the score MFMAs' lane group g (which feeds
+// dims 4 s + g, s = 0..31) reads 32 consecutive values.
 __host__ __device__ inline int pooled_dim_pos(int d) { return (d & 3) * 32 + (d >> 2); }
 
 // Row pitch (floats) of the transposed pooled V: n_v rounded up to 16, so
