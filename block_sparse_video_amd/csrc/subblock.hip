@@ -19,17 +19,19 @@
 // Text and audio keys stay dense and there is no coarse term.
 //
 // Stage 1 (subpool_kernel) writes the sub-block means of Q and K in the exact
-// per-lane order of the float64 MFMA operands of stage 2, so each operand
-// load there is a contiguous 1 KiB wavefront read.  Packed layout per head
-// and group c of four video tiles (16 sub-block rows j = 4 * (u % 4) + a):
+// per-lane order of the MFMA operands of stage 2, so each operand load there
+// is a contiguous 1 KiB wavefront read.  Packed layout per head and group c
+// of four video tiles (16 sub-block rows j = 4 * (u % 4) + a):
 //   [c][i = 0..7][lane = 16 g + j][e = 0..3] = mean of row j, dim 32 g + 4 i + e.
-// Stage 2 (subblock_route_kernel) is a float64 MFMA product Qs Ks^T per head
+// Stage 2 (subblock_route_kernel) is a float32 MFMA product Qs Ks^T per head
 // (16 x 16 x 4 tiles: four query tiles x four key tiles per output tile, the
-// 16 sub-block pairs of one tile pair in 4 lanes x 4 registers),
-// the log-sum-exp of each tile pair in registers, one row of scores per
-// query tile in LDS, and the wavefront top-k of topk_wave.h.  The score
-// arithmetic is float64 throughout, so selections agree with a float64
-// statement of the rule except where scores tie to rounding.
+// 16 sub-block pairs of one tile pair in 4 lanes x 4 registers), the float32
+// log-sum-exp of each tile pair in registers, one row of score slots per
+// query tile in LDS (each score with a proven bound on its distance from the
+// float64 score of the definition), and a wavefront top-k that takes every
+// key the bounds decide and ranks the undecided band by recomputed float64
+// scores.  Selections therefore agree with the float64 statement of the rule
+// except where float64 scores tie to rounding.
 #include "topk_wave.h"
 #include "vsa_internal.h"
 
@@ -38,7 +40,7 @@
 namespace vsa {
 namespace {
 
-typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -95,10 +97,11 @@ __global__ __launch_bounds__(128) void subpool_kernel(const uint16_t* __restrict
 
 // One 16-row group of packed sub-block means (Qs or Ks) as this lane's 32
 // float MFMA operands: element s is dim 32 (lane / 16) + s of row `row`
-// (lane % 16 for the B operand; a permuted row for the A operand).
-__device__ __forceinline__ void load_group(const float* __restrict__ base, int lane, int row,
-                                           float (&x)[32]) {
+// (lane % 16 for both operands).  Returns the sum of their squares.
+__device__ __forceinline__ float load_group(const float* __restrict__ base, int lane, int row,
+                                            float (&x)[32]) {
     const float4* p = (const float4*)base + ((lane & 48) | row);
+    float ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const float4 t = p[64 * i];
@@ -106,35 +109,297 @@ __device__ __forceinline__ void load_group(const float* __restrict__ base, int l
         x[4 * i + 1] = t.y;
         x[4 * i + 2] = t.z;
         x[4 * i + 3] = t.w;
+        ss = fmaf(t.x, t.x, fmaf(t.y, t.y, fmaf(t.z, t.z, fmaf(t.w, t.w, ss))));
     }
+    return ss;
 }
 
+// Largest |row| of the four sub-block rows of each tile of a 16-row group:
+// the four lane groups' partial sums of squares added (lanes 16 g + j hold
+// row j), then the maximum over the tile's rows j = 4 t .. 4 t + 3.  Every
+// lane returns the value of tile (lane % 16) / 4.
+__device__ __forceinline__ float tile_max_norm2(float ss) {
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    ss = fmaxf(ss, __shfl_xor(ss, 1));
+    return fmaxf(ss, __shfl_xor(ss, 2));
+}
+
+constexpr double kAlphaR = 0.088388347648318440550;  // 1/sqrt(128)
+
 // Log-sum-exp of the 16 sub-block logits of each tile pair in one 16 x 16
-// MFMA output tile.  The float64 16x16x4 MFMA leaves output row
-// l / 16 + 4 v of column l % 16 in register v of lane l; lane l of the A
-// operand therefore loads query sub-row sigma(l % 16), sigma(i) = 4 (i % 4) +
-// i / 4, so that register v of lane l holds query sub-block a = v of query
-// tile l / 16 against key sub-block l % 4 of key tile (l % 16) / 4.  The
-// pair's 16 values sit in 4 adjacent lanes; every lane returns its pair's
-// score.
-__device__ __forceinline__ double pair_lse(const f64x4& acc) {
-    constexpr double alpha = 0.088388347648318440550;  // 1/sqrt(128)
-    const double x0 = alpha * acc[0], x1 = alpha * acc[1];
-    const double x2 = alpha * acc[2], x3 = alpha * acc[3];
-    double m = fmax(fmax(x0, x1), fmax(x2, x3));
-    m = fmax(m, __shfl_xor(m, 1));
-    m = fmax(m, __shfl_xor(m, 2));
-    double e = exp(x0 - m) + exp(x1 - m) + exp(x2 - m) + exp(x3 - m);
+// output tile.  The float32 16x16x4 MFMA leaves output row 4 (l / 16) + v of
+// column l % 16 in register v of lane l; with the operand rows in their
+// natural order (row 4 t + a = sub-block a of tile t of the group), register
+// v of lane l holds query sub-block a = v of query tile l / 16 against key
+// sub-block l % 4 of key tile (l % 16) / 4.  The pair's 16 values sit in 4
+// adjacent lanes; every lane returns its pair's score.  Float32 throughout:
+// the logits rounded once, expf and logf within 3 ulp as OpenCL requires of
+// them; kLse32 bounds the result's error.
+__device__ __forceinline__ float pair_lse(const f32x4& acc) {
+    constexpr float alpha = (float)kAlphaR;
+    const float x0 = alpha * acc[0], x1 = alpha * acc[1];
+    const float x2 = alpha * acc[2], x3 = alpha * acc[3];
+    float m = fmaxf(fmaxf(x0, x1), fmaxf(x2, x3));
+    m = fmaxf(m, __shfl_xor(m, 1));
+    m = fmaxf(m, __shfl_xor(m, 2));
+    float e = expf(x0 - m) + expf(x1 - m) + expf(x2 - m) + expf(x3 - m);
     e += __shfl_xor(e, 1);
     e += __shfl_xor(e, 2);
+    return m + logf(e);
+}
+
+// Logits: each is one chain of 32 float32 MFMAs (128 products).  A 128-term
+// float32 dot product in any order and rounding mode is within gamma_128 =
+// 128u / (1 - 128u), u = 2^-23, of the sum of |products|, which
+// Cauchy-Schwarz bounds by |Qs[u][a]| |Ks[w][b]|; so every computed logit of
+// a tile pair is within
+//   alpha * kLogitErr * max_a |Qs[u][a]| * max_b |Ks[w][b]|
+// (+ a term for flushed denormals) of the float64 logit, and the log-sum-exp,
+// 1-Lipschitz in the max norm, moves by no more.  (Shorter chains added in
+// float64 narrow the bound but cost more than the recomputes they save.)
+constexpr double kLogitErr = 1.6e-5;  // gamma_128 = 1.526e-5; float32 norms
+constexpr double kLogitDenorm = 0x1p-117;
+// Error of the float32 log-sum-exp given its float64 logits, beside the
+// 2^-22 |score| of rounding the logits, the maximum and the final sum: the
+// differences x - m rounded (their relative 2^-24 |t| moves each term e^t by
+// at most 2^-24 / e of the sum, which is >= 1), expf and logf within 3 ulp,
+// 15 float32 additions of terms in (0, 1]; about 3.5e-6 in all, so 1e-5.  The
+// float64 recompute of a band key is within ~1e-15 of the definition.
+constexpr double kLse32 = 1e-5;
+
+template <int NG>
+__device__ __forceinline__ void logit_chains(const float (&a)[32], const float (&bq)[NG][32],
+                                             f32x4 (&acc)[NG]) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) acc[g] = (f32x4){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 32; ++s)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], bq[g][s], acc[g], 0, 0, 0);
+}
+
+// A score slot of the LDS rows: the stored float32 score (low word) and a
+// bound on its distance from the float64 score (high word, rounded up).
+__device__ __forceinline__ uint64_t pack_slot(float s, double bound) {
+    const float sf = s + 0.0f;
+    const double e = bound;
+    float ef = (float)e;
+    if ((double)ef < e) ef = __uint_as_float(__float_as_uint(ef) + 1u);  // round up (e >= 0)
+    if (!(e < 0x1p100)) ef = INFINITY;
+    return ((uint64_t)__float_as_uint(ef) << 32) | __float_as_uint(sf);
+}
+
+// The float64 score of (query tile u, key tile w) of one head, computed by
+// the whole wavefront: lane l forms logit p = l % 16 (query sub-block p / 4,
+// key sub-block p % 4) over dims 32 (l / 16) .. + 31, the four partial dot
+// products are added, and the 16 logits' max + log of summed exponentials
+// follows in float64.  Every lane returns the score.  q_h, k_h: the head's
+// packed sub-block means.
+__device__ double score_f64(const float* __restrict__ q_h, const float* __restrict__ k_h, int u,
+                            int w, int lane) {
+    const int p = lane & 15, c4 = lane >> 4;
+    const float* qr = q_h + (int64_t)(u >> 2) * 2048 + 64 * c4 + 4 * (4 * (u & 3) + (p >> 2));
+    const float* kr = k_h + (int64_t)(w >> 2) * 2048 + 64 * c4 + 4 * (4 * (w & 3) + (p & 3));
+    double dot = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 q4 = *(const float4*)(qr + 256 * i);
+        const float4 k4 = *(const float4*)(kr + 256 * i);
+        dot = __builtin_fma((double)q4.x, (double)k4.x, dot);
+        dot = __builtin_fma((double)q4.y, (double)k4.y, dot);
+        dot = __builtin_fma((double)q4.z, (double)k4.z, dot);
+        dot = __builtin_fma((double)q4.w, (double)k4.w, dot);
+    }
+    dot += __shfl_xor(dot, 16);
+    dot += __shfl_xor(dot, 32);
+    const double x = kAlphaR * dot;
+    double m = x;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) m = fmax(m, __shfl_xor(m, off));
+    double e = exp(x - m);
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) e += __shfl_xor(e, off);
     return m + log(e);
 }
 
+// Selection of one row (query tile u) from its score slots.  With E the
+// row's largest bound and T the k-th largest stored score, every key stored
+// above T + 2E is in the exact top k by float64 score and every key below
+// T - 2E is not (at least k keys have a float64 score >= T - E, at most
+// k - 1 one > T + E); the keys in between (the band) are ranked by their
+// recomputed float64 scores when they outnumber the places left, ties to the
+// lower index.  zero_q: every logit of the row is exactly 0, so every stored
+// score is the same value and the lowest k indices are the selection.
+template <int NS>
+__device__ void select_row_band(uint64_t* row, int n_v, int k, bool zero_q, int lane,
+                                const float* __restrict__ q_h, const float* __restrict__ k_h,
+                                int u, int32_t* __restrict__ out) {
+    static_assert(NS <= 128, "band masks hold 128 slots");
+    if (zero_q) {
+        for (int i = lane; i < k; i += 64) out[i] = i;
+        return;
+    }
+    uint32_t kv[NS];
+    float emax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int w = lane + 64 * i;
+        kv[i] = 0u;
+        if (w < n_v) {
+            const uint64_t sl = row[w];
+            kv[i] = order_key32(__uint_as_float((uint32_t)sl));
+            emax = fmaxf(emax, __uint_as_float((uint32_t)(sl >> 32)));
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) emax = fmaxf(emax, __shfl_xor(emax, off));
+    uint32_t gt;
+    const uint32_t t = kth_largest(kv, (uint32_t)k, gt);
+    uint32_t lo = 1u, hi = 0xFFFFFFFFu;
+    if (emax < 0x1p100f) {
+        const double T = (double)key32_value(t);
+        lo = key32_at_or_below(T - 2.0 * (double)emax);
+        hi = key32_at_or_above(T + 2.0 * (double)emax);
+    }
+    uint64_t above_m[2] = {0ull, 0ull}, band_m[2] = {0ull, 0ull};
+    uint32_t above = 0, band = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const bool ab = kv[i] > hi, bd = kv[i] != 0u && kv[i] >= lo && kv[i] <= hi;
+        above_m[i >> 6] |= (uint64_t)ab << (i & 63);
+        band_m[i >> 6] |= (uint64_t)bd << (i & 63);
+        above += (uint32_t)__popcll(__ballot(ab));
+        band += (uint32_t)__popcll(__ballot(bd));
+    }
+    uint32_t need = (uint32_t)k - above;
+    if (band < need) {
+        // cannot happen while the bounds hold: rank the whole row instead
+        above_m[0] = above_m[1] = band_m[0] = band_m[1] = 0ull;
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+            if (kv[i] != 0u) band_m[i >> 6] |= 1ull << (i & 63);
+        need = (uint32_t)k;
+        band = (uint32_t)n_v;
+    }
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    if (band == need) {
+        uint32_t outc = 0;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const bool take = ((above_m[i >> 6] | band_m[i >> 6]) >> (i & 63)) & 1ull;
+            const uint64_t tm = __ballot(take);
+            const uint32_t pos = outc + (uint32_t)__popcll(tm & lt_mask);
+            if (take && pos < (uint32_t)k) out[pos] = lane + 64 * i;
+            outc += (uint32_t)__popcll(tm);
+        }
+        return;
+    }
+    // the band's float64 scores are recomputed, member j's (order key, index)
+    // kept in lane j, and member j is taken if fewer than `need` members come
+    // before it in the order (score desc, index asc); its slot then holds 1,
+    // else 0 (this wavefront owns the row).  A band of more than 64 keys
+    // (rows of nearly equal scores) is ranked by bisection on the recomputed
+    // keys held in the slots.
+    auto in_band = [&](int i) -> bool { return ((i < 64 ? band_m[0] : band_m[1]) >> (i & 63)) & 1ull; };
+    uint64_t mkey = 0ull;
+    int mw = 0x7FFFFFFF;
+    uint32_t nb = 0;
+#pragma unroll 1
+    for (int i = 0; i < NS; ++i) {
+        uint64_t todo = __ballot(in_band(i));
+        while (todo) {
+            const int ln = __builtin_ctzll(todo);  // wave-uniform
+            todo &= todo - 1ull;
+            const int w = ln + 64 * i;
+            const uint64_t key = order_key(score_f64(q_h, k_h, u, w, lane) + 0.0);
+            if (band <= 64) {
+                if (lane == (int)nb) {
+                    mkey = key;
+                    mw = w;
+                }
+            } else if (lane == ln) {
+                row[w] = key;
+            }
+            ++nb;
+        }
+    }
+    if (band <= 64) {
+        uint32_t before = 0;
+        for (uint32_t j = 0; j < nb; ++j) {
+            const uint64_t kj = __shfl(mkey, (int)j);
+            const int wj = __shfl(mw, (int)j);
+            before += (kj > mkey || (kj == mkey && wj < mw)) ? 1u : 0u;
+        }
+        if ((uint32_t)lane < nb) row[mw] = before < need ? 1ull : 0ull;
+    } else {
+        uint64_t bmin = ~0ull, bmax = 0ull;
+#pragma unroll 1
+        for (int i = 0; i < NS; ++i)
+            if (in_band(i)) {
+                const uint64_t key = row[lane + 64 * i];
+                bmin = key < bmin ? key : bmin;
+                bmax = key > bmax ? key : bmax;
+            }
+#pragma unroll 1
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint64_t x = __shfl_xor(bmin, off), y = __shfl_xor(bmax, off);
+            bmin = x < bmin ? x : bmin;
+            bmax = y > bmax ? y : bmax;
+        }
+        bmin = uniform_key(bmin);
+        bmax = uniform_key(bmax);
+        auto count_ge = [&](uint64_t th) -> uint32_t {
+            uint32_t c = 0;
+#pragma unroll 1
+            for (int i = 0; i < NS; ++i)
+                c += (uint32_t)__popcll(__ballot(in_band(i) && row[lane + 64 * i] >= th));
+            return c;
+        };
+        // the need-th largest band key: the largest th with count_ge(th) >= need
+        uint64_t blo = bmin, bhi = bmax;
+        while (blo < bhi) {
+            const uint64_t mid = blo + ((bhi - blo + 1) >> 1);
+            if (count_ge(mid) >= need) blo = mid;
+            else bhi = mid - 1;
+        }
+        uint32_t bgt = 0;
+#pragma unroll 1
+        for (int i = 0; i < NS; ++i)
+            bgt += (uint32_t)__popcll(__ballot(in_band(i) && row[lane + 64 * i] > blo));
+        const uint32_t take_eq = need - bgt;  // band keys equal to blo to take, lowest index first
+        uint32_t eqseen = 0;
+#pragma unroll 1
+        for (int i = 0; i < NS; ++i) {
+            const int w = lane + 64 * i;
+            const bool bd = in_band(i);
+            const uint64_t key = bd ? row[w] : 0ull;
+            const bool eq = bd && key == blo;
+            const uint64_t em = __ballot(eq);
+            const uint32_t erank = eqseen + (uint32_t)__popcll(em & lt_mask);
+            if (bd) row[w] = (key > blo || (eq && erank < take_eq)) ? 1ull : 0ull;
+            eqseen += (uint32_t)__popcll(em);
+        }
+    }
+    uint32_t outc = 0;
+#pragma unroll 1
+    for (int i = 0; i < NS; ++i) {
+        const int w = lane + 64 * i;
+        const bool ab = ((i < 64 ? above_m[0] : above_m[1]) >> (i & 63)) & 1ull;
+        const bool take = ab || (in_band(i) && row[w] == 1ull);
+        const uint64_t tm = __ballot(take);
+        const uint32_t pos = outc + (uint32_t)__popcll(tm & lt_mask);
+        if (take && pos < (uint32_t)k) out[pos] = w;
+        outc += (uint32_t)__popcll(tm);
+    }
+}
+
 // grid (H * ceil(n_c / RT)), 512 threads = 8 wavefronts.  A workgroup owns
-// RT groups of four query tiles of one head (4 RT rows of scores in LDS).
-// Wavefront wv multiplies query group wv % RT against the key groups c with
-// c % (8 / RT) == wv / RT, four key groups per step (four independent MFMA
-// chains; two, then one, for the remainder), and stores the scores; then
+// RT groups of four query tiles of one head (4 RT rows of score slots in
+// LDS).  Wavefront wv multiplies query group wv % RT against the key groups
+// c with c % (8 / RT) == wv / RT, four key groups per step (four independent
+// MFMA chains; two, then one, for the remainder), and stores the slots; then
 // each wavefront selects rows wv, wv + 8.
 // Blocks are mapped so that each XCD walks a contiguous, head-major range of
 // (head, query block) items: the key means of one head (n_c * 8 KiB) stay in
@@ -145,7 +410,7 @@ __global__ __launch_bounds__(512) void subblock_route_kernel(const float* __rest
                                                              int H, int n_v, int n_c, int k,
                                                              int ldw, int32_t* __restrict__ sel) {
     extern __shared__ __align__(16) unsigned char smem[];
-    double* sc = (double*)smem;  // [4 RT][ldw]
+    uint64_t* sc = (uint64_t*)smem;  // [4 RT][ldw] score slots
     constexpr int PH = 8 / RT;
     const int nub = (n_c + RT - 1) / RT;
     const int64_t items = (int64_t)H * nub;
@@ -159,79 +424,85 @@ __global__ __launch_bounds__(512) void subblock_route_kernel(const float* __rest
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int rt = wv % RT, ph = wv / RT;
     const int cq = ub * RT + rt;
+    const float* qh = qsub + (int64_t)h * n_c * 2048;
+    const float* kh = ksub + (int64_t)h * n_c * 2048;
 
     if (cq < n_c) {
         float a[32];
-        const int arow = ((lane & 3) << 2) | ((lane >> 2) & 3);  // sigma(lane % 16)
-        load_group(qsub + ((int64_t)h * n_c + cq) * 2048, lane, arow, a);
+        const int arow = lane & 15;
+        float qq = load_group(qh + (int64_t)cq * 2048, lane, arow, a);
         // rows of query tiles past n_v (last group) are zero
         if (4 * cq + (arow >> 2) >= n_v) {
 #pragma unroll
             for (int s = 0; s < 32; ++s) a[s] = 0.0f;
+            qq = 0.0f;
         }
-        const float* kh = ksub + (int64_t)h * n_c * 2048;
-        const int uq = 4 * cq + (lane >> 4);  // this lane's query tile
+        // max_a |Qs[u][a]| of this lane's output query tile, lane / 16
+        const double qmax = sqrt((double)__shfl(tile_max_norm2(qq), 4 * (lane >> 4)));
+        const int uq = 4 * cq + (lane >> 4);
         const int lrow = 4 * rt + (lane >> 4);
         const bool store_lane = (lane & 3) == 0 && uq < n_v;
-        auto finish = [&](const f64x4& acc, int c) {
-            const double s = pair_lse(acc);
+        // kn: max_b |Ks[w][b]| of this lane's output key tile, (lane % 16) / 4
+        auto finish = [&](const f32x4& acc, int c, double kn) {
+            const float s = pair_lse(acc);
             const int w = 4 * c + ((lane & 15) >> 2);
-            if (store_lane && w < n_v) sc[lrow * ldw + w] = s + 0.0;
+            if (store_lane && w < n_v) {
+                const double qk = qmax * kn;
+                const double bound = kAlphaR * (kLogitErr * qk + kLogitDenorm * (qmax + kn + 1.0)) +
+                                     kLse32 + 0x1p-22 * fabs((double)s);
+                sc[lrow * ldw + w] = pack_slot(s, qk < 0x1p100 ? bound : INFINITY);
+            }
         };
+        // key groups: the packed means of tiles past n_v are zero (subpool)
+        auto load_keys = [&](int c, float (&bq)[32]) -> double {
+            return sqrt((double)tile_max_norm2(load_group(kh + (int64_t)c * 2048, lane, lane & 15, bq)));
+        };
+        auto issue_keys = [&](int c, float (&bq)[32]) {
+            const float4* p = (const float4*)(kh + (int64_t)c * 2048) + ((lane & 48) | (lane & 15));
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 t = p[64 * i];
+                bq[4 * i + 0] = t.x;
+                bq[4 * i + 1] = t.y;
+                bq[4 * i + 2] = t.z;
+                bq[4 * i + 3] = t.w;
+            }
+        };
+        auto key_norm = [&](const float (&bq)[32]) -> double {
+            float ss = 0.0f;
+#pragma unroll
+            for (int s = 0; s < 32; ++s) ss = fmaf(bq[s], bq[s], ss);
+            return sqrt((double)tile_max_norm2(ss));
+        };
+        // two key groups per step; the next step's groups are loaded while
+        // this step's log-sum-exps run
         int c = ph;
-        for (; c + 3 * PH < n_c; c += 4 * PH) {
-            float bq[4][32];
+        {
+            float bq[2][32];
+            if (c + PH < n_c)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                load_group(kh + (int64_t)(c + gq * PH) * 2048, lane, lane & 15, bq[gq]);
-                if (4 * (c + gq * PH) + ((lane & 15) >> 2) >= n_v) {
+                for (int gq = 0; gq < 2; ++gq) issue_keys(c + gq * PH, bq[gq]);
+            for (; c + PH < n_c; c += 2 * PH) {
+                double kn[2];
 #pragma unroll
-                    for (int s = 0; s < 32; ++s) bq[gq][s] = 0.0f;
-                }
+                for (int gq = 0; gq < 2; ++gq) kn[gq] = key_norm(bq[gq]);
+                f32x4 accq[2];
+                logit_chains<2>(a, bq, accq);
+                __builtin_amdgcn_sched_barrier(0);
+                if (c + 3 * PH < n_c)
+#pragma unroll
+                    for (int gq = 0; gq < 2; ++gq) issue_keys(c + (2 + gq) * PH, bq[gq]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int gq = 0; gq < 2; ++gq) finish(accq[gq], c + gq * PH, kn[gq]);
             }
-            f64x4 accq[4];
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) accq[gq] = (f64x4){0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-            for (int s = 0; s < 32; ++s) {
-                const double as = (double)a[s];
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq)
-                    accq[gq] = __builtin_amdgcn_mfma_f64_16x16x4f64(as, (double)bq[gq][s], accq[gq], 0, 0, 0);
-            }
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) finish(accq[gq], c + gq * PH);
-        }
-        for (; c + PH < n_c; c += 2 * PH) {
-            float b0[32], b1[32];
-            load_group(kh + (int64_t)c * 2048, lane, lane & 15, b0);
-            load_group(kh + (int64_t)(c + PH) * 2048, lane, lane & 15, b1);
-            if (4 * (c + PH) + ((lane & 15) >> 2) >= n_v) {
-#pragma unroll
-                for (int s = 0; s < 32; ++s) b1[s] = 0.0f;
-            }
-            f64x4 acc0 = {0.0, 0.0, 0.0, 0.0}, acc1 = acc0;
-#pragma unroll
-            for (int s = 0; s < 32; ++s) {
-                const double as = (double)a[s];
-                acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(as, (double)b0[s], acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(as, (double)b1[s], acc1, 0, 0, 0);
-            }
-            finish(acc0, c);
-            finish(acc1, c + PH);
         }
         if (c < n_c) {
-            float b0[32];
-            load_group(kh + (int64_t)c * 2048, lane, lane & 15, b0);
-            if (4 * c + ((lane & 15) >> 2) >= n_v) {
-#pragma unroll
-                for (int s = 0; s < 32; ++s) b0[s] = 0.0f;
-            }
-            f64x4 acc0 = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-            for (int s = 0; s < 32; ++s)
-                acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)a[s], (double)b0[s], acc0, 0, 0, 0);
-            finish(acc0, c);
+            float bq[1][32];
+            const double kn0 = load_keys(c, bq[0]);
+            f32x4 accq[1];
+            logit_chains<1>(a, bq, accq);
+            finish(accq[0], c, kn0);
         }
     }
     __syncthreads();
@@ -240,10 +511,19 @@ __global__ __launch_bounds__(512) void subblock_route_kernel(const float* __rest
     for (int r = wv; r < 4 * RT; r += 8) {
         const int u = 4 * ub * RT + r;
         if (u >= n_v) break;
-        const double* row = sc + r * ldw;
-        uint32_t need = 0;
-        const uint64_t kth = kth_key_bisect<NS>(row, n_v, k, lane, need);
-        emit_topk(row, n_v, k, kth, need, lane, sel + ((int64_t)h * n_v + u) * k);
+        // is the whole query tile zero (every logit of the row exactly 0)?
+        // (lane 4 g + a < 16 reads dims 32 g + 4 i .. + 3 of sub-block a)
+        const float* qg = qh + (int64_t)(u >> 2) * 2048 + 16 * (u & 3);
+        bool nz = false;
+        if (lane < 16)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 t = *(const float4*)(qg + i * 256 + 64 * (lane >> 2) + 4 * (lane & 3));
+                nz |= t.x != 0.0f || t.y != 0.0f || t.z != 0.0f || t.w != 0.0f;
+            }
+        const bool zero_q = __ballot(nz) == 0ull;
+        select_row_band<NS>(sc + r * ldw, n_v, k, zero_q, lane, qh, kh, u,
+                            sel + ((int64_t)h * n_v + u) * k);
     }
 }
 
@@ -252,7 +532,7 @@ hipError_t launch_route(const Shape& s, int32_t* sel, const uint8_t* ws, const L
                         hipStream_t stream) {
     const int n_c = (s.n_v + 3) / 4;
     const int ldw = (s.n_v + 3) & ~3;
-    const size_t lds = (size_t)4 * RT * ldw * sizeof(double);
+    const size_t lds = (size_t)4 * RT * ldw * sizeof(uint64_t);
     static std::atomic<size_t> lds_allowed[kMaxDevices];
     hipError_t e = ensure_dynamic_lds((const void*)subblock_route_kernel<RT, NS>, lds_allowed, lds);
     if (e != hipSuccess) return e;

@@ -1,8 +1,8 @@
-// topk_wave.h -- exact top-k of one row of float64 scores by one wavefront:
-// order-preserving 64-bit keys, the k-th largest key by bisection with the
-// row held in registers, and the compaction that writes the selected indices
-// in ascending order, tied keys taken by lowest index.  Used by both tile
-// selection rules (the pooled tile score and the SubBlock router).
+// topk_wave.h -- exact top-k of one row of scores by one wavefront:
+// order-preserving 32- and 64-bit keys, the k-th largest key by bisection with
+// the row held in registers, and the compaction that writes the selected
+// indices in ascending order, tied keys taken by lowest index.  Used by both
+// tile selection rules (the pooled tile score and the SubBlock router).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -17,6 +17,76 @@ namespace {
 __device__ __forceinline__ uint64_t order_key(double x) {
     const uint64_t b = (uint64_t)__double_as_longlong(x);
     return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// Order-preserving map of a float32 to uint32 (key 0 is never a finite score).
+// Consecutive keys are consecutive floats (-0 and +0 apart), so key + 1 is
+// the next float up.
+__device__ __forceinline__ uint32_t order_key32(float x) {
+    const uint32_t b = __float_as_uint(x);
+    return (b >> 31) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key32_value(uint32_t key) {
+    return __uint_as_float((key >> 31) ? (key & 0x7FFFFFFFu) : ~key);
+}
+// Smallest key whose float is >= x, and largest whose float is <= x.
+__device__ __forceinline__ uint32_t key32_at_or_above(double x) {
+    const float f = (float)x + 0.0f;
+    return order_key32(f) + ((double)f < x ? 1u : 0u);
+}
+__device__ __forceinline__ uint32_t key32_at_or_below(double x) {
+    const float f = (float)x + 0.0f;
+    return order_key32(f) - ((double)f > x ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t uniform_key(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)x);
+}
+__device__ __forceinline__ uint64_t uniform_key(uint64_t x) {
+    return ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+}
+
+// The kk-th largest of the keys a wavefront holds (kk >= 1, at least kk keys
+// nonzero; zero keys are absent), by bisection on the key value; `gt`
+// returns the number of keys above it.
+template <typename Key, int NS>
+__device__ __forceinline__ Key kth_largest(const Key (&kv)[NS], uint32_t kk, uint32_t& gt) {
+    Key kmin = ~(Key)0, kmax = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        kmax = kv[i] > kmax ? kv[i] : kmax;
+        kmin = (kv[i] != 0 && kv[i] < kmin) ? kv[i] : kmin;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const Key a = __shfl_xor(kmin, off), b = __shfl_xor(kmax, off);
+        kmin = a < kmin ? a : kmin;
+        kmax = b > kmax ? b : kmax;
+    }
+    // every lane now holds the same range: make it wave-uniform, so that the
+    // search below runs on the scalar unit
+    kmin = uniform_key(kmin);
+    kmax = uniform_key(kmax);
+    auto count_ge = [&](Key th) -> uint32_t {
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < NS; ++i) c += (uint32_t)__popcll(__ballot(kv[i] >= th));
+        return c;
+    };
+    // the answer is the largest T with count_ge(T) >= kk, a key value in
+    // [kmin, kmax]; invariant: count_ge(lo) >= kk and the answer is <= hi
+    Key lo = kmin, hi = kmax;
+    while (lo < hi) {
+        const Key mid = lo + (Key)((hi - lo + 1) >> 1);
+        if (count_ge(mid) >= kk) lo = mid;
+        else hi = mid - 1;
+    }
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) c += (uint32_t)__popcll(__ballot(kv[i] > lo));
+    gt = c;
+    return lo;
 }
 
 // Exact k-th largest of one row's keys by bisection on the 64-bit key value,

@@ -161,6 +161,50 @@ def test_copied_key_tiles_tie_exactly():
     full_check(x, s_t, s_v, s_a, 0.7, exempt_ok=False)
 
 
+def test_near_triples_ranked_in_float64():
+    """Key tiles 3i + 1 and 3i + 2 copy tile 3i with one token's dimension 0
+    moved by one and two bf16 steps, so the three scores differ by ~1e-9 to
+    ~1e-6: inside the band that the router's float32 products and
+    log-sum-exp leave undecided, far above float64 rounding.  With k = 8 the
+    cut of every row falls inside a triple and is resolved by the recomputed
+    float64 scores.  Exact match required."""
+    announce("subblock near triples: h=2 tiles=(1,40,1) sp=0.75")
+    h, s_t, n_v, s_a = 2, 64, 40, 64
+    s_v = n_v * T
+    x = synth.vsa_inputs(25, h, s_t, s_v, s_a)
+    k = x["k"].copy()
+    for w in range(0, n_v - 2, 3):
+        a = s_t + w * T
+        for j, step in ((1, 1), (2, 2)):
+            k[a + j * T: a + (j + 1) * T] = k[a: a + T]
+            bits = k[a + j * T + 5, :, 0].astype(np.int32)
+            k[a + j * T + 5, :, 0] = (bits + step).astype(np.uint16)
+    x["k"] = k
+    ref, _, _ = full_check(x, s_t, s_v, s_a, 0.75, exempt_ok=False)
+    kk = ref["k"]
+    s = -np.sort(-ref["scores"].reshape(-1, n_v), axis=1)
+    gap = s[:, kk - 1] - s[:, kk]
+    # the construction does what it says: every row is cut inside a triple
+    assert np.sum((gap > 0) & (gap < 1e-5)) == h * n_v, np.sort(gap)[-12:]
+
+
+def test_all_key_tiles_equal():
+    """Every key tile a copy of the first and Q nonzero: every score of a row
+    is the same value on both sides (a band of all 100 keys, more than a
+    wavefront's lanes), and the lowest k indices win.  Exact match
+    required."""
+    announce("subblock identical key tiles: h=1 tiles=(1,100,1)")
+    h, s_t, n_v, s_a = 1, 64, 100, 64
+    s_v = n_v * T
+    x = synth.vsa_inputs(26, h, s_t, s_v, s_a)
+    k = x["k"].copy()
+    for w in range(1, n_v):
+        k[s_t + w * T: s_t + (w + 1) * T] = k[s_t: s_t + T]
+    x["k"] = k
+    ref, _, sel = full_check(x, s_t, s_v, s_a, 0.75, exempt_ok=False)
+    assert np.array_equal(sel, np.broadcast_to(np.arange(ref["k"]), sel.shape))
+
+
 def test_zero_queries_take_lowest_indices():
     announce("subblock Q = 0: every score log 16")
     h, s_t, n_v, s_a = 2, 64, 40, 64
