@@ -39,7 +39,6 @@ D = 128
 FLOP_PER_PAIR = 4 * TILE * TILE * D          # QK^T + PV of one 64x64 tile pair
 PEAK_BF16_TFLOPS = 2500.0                   # MI355X dense bf16 MFMA (published)
 PEAK_HBM_GBS = 8000.0                       # MI355X HBM3E (published)
-PEAK_FP64_TFLOPS = 78.6                     # MI355X dense fp64 MFMA (published)
 PEAK_FP32_MFMA_TFLOPS = 157.3               # MI355X dense fp32 MFMA (published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fine_attn_traffic_10s_56h.txt")
 FINE_SOURCE = os.path.join(ROOT, "block_sparse_video_amd", "csrc", "fine_attn.hip")
@@ -287,11 +286,11 @@ def subblock_leg(bsv, torch, xd, shape, steps, warmup):
     fwd_ms = ev[1].elapsed_time(ev[2]) / steps
     kk = bsv.vsa_subblock_count(s_v, sp)
     n_v = s_v // TILE
-    route_flop = 2.0 * h * (4 * n_v) ** 2 * D  # float64 MFMA work of the scores
+    route_flop = 2.0 * h * (4 * n_v) ** 2 * D  # float32 MFMA work of the logits
     flops = tile_pairs(h, s_t, s_v, s_a, kk) * FLOP_PER_PAIR
     return {"workload": f"SubBlock router path, same inputs, sparsity {sp} (k={kk})",
-            "k": kk, "router_ms": sel_ms, "router_fp64_tflops": route_flop / (sel_ms * 1e-3) / 1e12,
-            "router_fp64_frac": route_flop / (sel_ms * 1e-3) / 1e12 / PEAK_FP64_TFLOPS,
+            "k": kk, "router_ms": sel_ms, "router_tflops": route_flop / (sel_ms * 1e-3) / 1e12,
+            "router_frac_of_fp32_mfma_157.3": route_flop / (sel_ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS,
             "ms_per_layer": fwd_ms, "tflops_computed_tiles": flops / (fwd_ms * 1e-3) / 1e12,
             "steps": steps}
 
@@ -326,7 +325,7 @@ def subblock_whole_leg(bsv, torch, xd, shape, steps, warmup):
     flops = float(h) * n * kk * FLOP_PER_PAIR
     return {"workload": f"SubBlock router over the whole sequence, same inputs, sparsity {sp} "
                         f"(k={kk} of {n} tiles per query tile)",
-            "k": kk, "router_ms": sel_ms, "router_fp64_tflops": route_flop / (sel_ms * 1e-3) / 1e12,
+            "k": kk, "router_ms": sel_ms, "router_tflops": route_flop / (sel_ms * 1e-3) / 1e12,
             "ms_per_layer": fwd_ms, "tflops_computed_tiles": flops / (fwd_ms * 1e-3) / 1e12,
             "steps": steps}
 
@@ -469,7 +468,7 @@ def main():
                    "arch": getattr(prop, "gcnArchName", ""),
                    "peak_clock_mhz": device_clock_mhz(),
                    "peak_used": {"bf16_mfma_tflops": PEAK_BF16_TFLOPS,
-                                 "fp64_mfma_tflops": PEAK_FP64_TFLOPS,
+                                 "fp32_mfma_tflops": PEAK_FP32_MFMA_TFLOPS,
                                  "hbm_gbs": PEAK_HBM_GBS}},
     }
     del r
