@@ -203,7 +203,7 @@ __device__ double score_f64(const float* __restrict__ q_h, const float* __restri
     const float* qr = q_h + (int64_t)(u >> 2) * 2048 + 64 * c4 + 4 * (4 * (u & 3) + (p >> 2));
     const float* kr = k_h + (int64_t)(w >> 2) * 2048 + 64 * c4 + 4 * (4 * (w & 3) + (p & 3));
     double dot = 0.0;
-#pragma unroll
+#pragma unroll 2
     for (int i = 0; i < 8; ++i) {
         const float4 q4 = *(const float4*)(qr + 256 * i);
         const float4 k4 = *(const float4*)(kr + 256 * i);
@@ -398,14 +398,17 @@ __device__ void select_row_band(uint64_t* row, int n_v, int k, bool zero_q, int 
 // grid (H * ceil(n_c / RT)), 512 threads = 8 wavefronts.  A workgroup owns
 // RT groups of four query tiles of one head (4 RT rows of score slots in
 // LDS).  Wavefront wv multiplies query group wv % RT against the key groups
-// c with c % (8 / RT) == wv / RT, four key groups per step (four independent
-// MFMA chains; two, then one, for the remainder), and stores the slots; then
-// each wavefront selects rows wv, wv + 8.
+// c with c % (8 / RT) == wv / RT, one key group per step with the next
+// step's group loaded while this step's log-sum-exps run, and stores the
+// slots; then each wavefront selects rows wv, wv + 8.  MINB workgroups share
+// a CU (the registers are capped for it): with two, one workgroup's top-k
+// runs beside the other's matrix work.
 // Blocks are mapped so that each XCD walks a contiguous, head-major range of
 // (head, query block) items: the key means of one head (n_c * 8 KiB) stay in
 // that XCD's L2 while its CUs share them.
-template <int RT, int NS>
-__global__ __launch_bounds__(512) void subblock_route_kernel(const float* __restrict__ qsub,
+template <int RT, int NS, int MINB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2 * MINB))) void
+subblock_route_kernel(const float* __restrict__ qsub,
                                                              const float* __restrict__ ksub,
                                                              int H, int n_v, int n_c, int k,
                                                              int ldw, int32_t* __restrict__ sel) {
@@ -454,9 +457,6 @@ __global__ __launch_bounds__(512) void subblock_route_kernel(const float* __rest
             }
         };
         // key groups: the packed means of tiles past n_v are zero (subpool)
-        auto load_keys = [&](int c, float (&bq)[32]) -> double {
-            return sqrt((double)tile_max_norm2(load_group(kh + (int64_t)c * 2048, lane, lane & 15, bq)));
-        };
         auto issue_keys = [&](int c, float (&bq)[32]) {
             const float4* p = (const float4*)(kh + (int64_t)c * 2048) + ((lane & 48) | (lane & 15));
 #pragma unroll
@@ -474,35 +474,18 @@ __global__ __launch_bounds__(512) void subblock_route_kernel(const float* __rest
             for (int s = 0; s < 32; ++s) ss = fmaf(bq[s], bq[s], ss);
             return sqrt((double)tile_max_norm2(ss));
         };
-        // two key groups per step; the next step's groups are loaded while
-        // this step's log-sum-exps run
-        int c = ph;
-        {
-            float bq[2][32];
-            if (c + PH < n_c)
-#pragma unroll
-                for (int gq = 0; gq < 2; ++gq) issue_keys(c + gq * PH, bq[gq]);
-            for (; c + PH < n_c; c += 2 * PH) {
-                double kn[2];
-#pragma unroll
-                for (int gq = 0; gq < 2; ++gq) kn[gq] = key_norm(bq[gq]);
-                f32x4 accq[2];
-                logit_chains<2>(a, bq, accq);
-                __builtin_amdgcn_sched_barrier(0);
-                if (c + 3 * PH < n_c)
-#pragma unroll
-                    for (int gq = 0; gq < 2; ++gq) issue_keys(c + (2 + gq) * PH, bq[gq]);
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int gq = 0; gq < 2; ++gq) finish(accq[gq], c + gq * PH, kn[gq]);
-            }
-        }
-        if (c < n_c) {
-            float bq[1][32];
-            const double kn0 = load_keys(c, bq[0]);
-            f32x4 accq[1];
-            logit_chains<1>(a, bq, accq);
-            finish(accq[0], c, kn0);
+        // one key group per step; the next step's group is loaded while this
+        // step's log-sum-exps run
+        float bq[1][32];
+        if (ph < n_c) issue_keys(ph, bq[0]);
+        for (int c = ph; c < n_c; c += PH) {
+            const double kn = key_norm(bq[0]);
+            f32x4 acc[1];
+            logit_chains<1>(a, bq, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            if (c + PH < n_c) issue_keys(c + PH, bq[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            finish(acc[0], c, kn);
         }
     }
     __syncthreads();
@@ -527,17 +510,17 @@ __global__ __launch_bounds__(512) void subblock_route_kernel(const float* __rest
     }
 }
 
-template <int RT, int NS>
+template <int RT, int NS, int MINB>
 hipError_t launch_route(const Shape& s, int32_t* sel, const uint8_t* ws, const Layout& L,
                         hipStream_t stream) {
     const int n_c = (s.n_v + 3) / 4;
     const int ldw = (s.n_v + 3) & ~3;
     const size_t lds = (size_t)4 * RT * ldw * sizeof(uint64_t);
     static std::atomic<size_t> lds_allowed[kMaxDevices];
-    hipError_t e = ensure_dynamic_lds((const void*)subblock_route_kernel<RT, NS>, lds_allowed, lds);
+    hipError_t e = ensure_dynamic_lds((const void*)subblock_route_kernel<RT, NS, MINB>, lds_allowed, lds);
     if (e != hipSuccess) return e;
     const int64_t blocks = (int64_t)s.H * ((n_c + RT - 1) / RT);
-    hipLaunchKernelGGL((subblock_route_kernel<RT, NS>), dim3((unsigned)blocks), dim3(512), lds,
+    hipLaunchKernelGGL((subblock_route_kernel<RT, NS, MINB>), dim3((unsigned)blocks), dim3(512), lds,
                        stream, (const float*)(ws + L.qsub), (const float*)(ws + L.ksub), s.H,
                        s.n_v, n_c, s.k, ldw, sel);
     return hipGetLastError();
@@ -553,10 +536,11 @@ hipError_t launch_subblock_route(const uint16_t* q, const uint16_t* k, const Sha
                        s.H, s.ldh, s.S_t, s.n_v, n_c, (float*)(ws + L.qsub), (float*)(ws + L.ksub));
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // rows of 4 RT query tiles x ldw float64 scores must fit the 160 KiB of LDS
-    if (s.n_v <= 1280) return launch_route<4, 20>(s, sel, ws, L, stream);
-    if (s.n_v <= 2560) return launch_route<2, 40>(s, sel, ws, L, stream);
-    return launch_route<1, 80>(s, sel, ws, L, stream);
+    // rows of 4 RT query tiles x ldw 8-byte score slots must fit the LDS:
+    // two workgroups per CU (80 KiB each) up to 1,280 tiles, then one
+    if (s.n_v <= 1280) return launch_route<2, 20, 2>(s, sel, ws, L, stream);
+    if (s.n_v <= 2560) return launch_route<2, 40, 1>(s, sel, ws, L, stream);
+    return launch_route<1, 80, 1>(s, sel, ws, L, stream);
 }
 
 }  // namespace vsa
