@@ -137,6 +137,10 @@ constexpr double kAlphaR = 0.088388347648318440550;  // 1/sqrt(128)
 // the logits rounded once, expf and logf within 3 ulp as OpenCL requires of
 // them; kLse32 bounds the result's error.
 __device__ __forceinline__ float pair_lse(const f32x4& acc) {
+    // no multiply-add contraction: x - m must subtract the rounded logits the
+    // maximum was taken over (fused, the maximum's own term would be its
+    // product's rounding error, which overflows exp at large magnitudes)
+#pragma clang fp contract(off)
     constexpr float alpha = (float)kAlphaR;
     const float x0 = alpha * acc[0], x1 = alpha * acc[1];
     const float x2 = alpha * acc[2], x3 = alpha * acc[3];
@@ -199,6 +203,7 @@ __device__ __forceinline__ uint64_t pack_slot(float s, double bound) {
 // packed sub-block means.
 __device__ double score_f64(const float* __restrict__ q_h, const float* __restrict__ k_h, int u,
                             int w, int lane) {
+#pragma clang fp contract(off)  // as in pair_lse: x - m on the rounded logits
     const int p = lane & 15, c4 = lane >> 4;
     const float* qr = q_h + (int64_t)(u >> 2) * 2048 + 64 * c4 + 4 * (4 * (u & 3) + (p >> 2));
     const float* kr = k_h + (int64_t)(w >> 2) * 2048 + 64 * c4 + 4 * (4 * (w & 3) + (p & 3));

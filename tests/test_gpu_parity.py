@@ -208,6 +208,33 @@ def test_close_pairs_decided_in_float64(log2_w0):
         assert tied >= n_v, tied
 
 
+def test_huge_magnitudes_rank_every_key_in_float64():
+    """Q and K scaled by 2^52 (exact in bf16): |Qbar_u| max|Kbar_w| exceeds
+    2^100, where the float32 score products could leave their range, so
+    every row is ranked by recomputed float64 scores.  Selection must match
+    the oracle exactly (the coarse branch is not checked: its float32 score
+    rows cannot hold these magnitudes to the bar)."""
+    announce("huge magnitudes: h=2 tiles=(1,70,1) frac=0.2, Q and K x 2^52")
+    h, s_t, n_v, s_a = 2, 64, 70, 64
+    s_v = n_v * T
+    x = synth.vsa_inputs(27, h, s_t, s_v, s_a)
+    for n in ("q", "k"):
+        x[n] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x[n]) * np.float32(2.0 ** 52))
+    xd = G.inputs_to_dev(x)
+    kk = bsv.vsa_topk_count(s_v, 0.2)
+    ws = torch.empty(bsv.vsa_workspace_bytes(h, s_t, s_v, s_a, 0.2), dtype=torch.uint8, device="cuda")
+    sel = torch.full((h, n_v, kk), -7, dtype=torch.int32, device="cuda")
+    bsv.vsa_pool_pack(xd["q"], xd["k"], xd["v"], s_t, s_v, s_a, ws)
+    bsv.vsa_select_coarse(h, s_t, s_v, s_a, 0.2, sel, ws)
+    torch.cuda.synchronize()
+    ref = oracle.select_coarse(x["q"], x["k"], x["v"], s_t, s_v, s_a, 0.2)
+    w = G.read_workspace(ws, h, s_t, s_v, s_a)
+    qn = np.linalg.norm(w["qbar64"], axis=-1).min()
+    kn = np.linalg.norm(w["kbar"].astype(np.float64), axis=-1).max()
+    assert qn * kn > 2.0 ** 100, (qn, kn)
+    G.check_selection(sel.cpu().numpy(), ref, exempt_ok=False)
+
+
 def test_longest_rows_of_the_matrix_core_select():
     """n_v = 1,280 video tiles, the most the matrix-core select kernel takes
     (20 keys per lane in its top-k, 82 KiB of float32 score rows, one

@@ -205,6 +205,32 @@ def test_all_key_tiles_equal():
     assert np.array_equal(sel, np.broadcast_to(np.arange(ref["k"]), sel.shape))
 
 
+def test_huge_magnitudes_rank_every_key_in_float64():
+    """Q and K scaled by 2^52 (exact in bf16): the logit bounds exceed 2^100,
+    so every key of every row is in the band, more than 64 keys are ranked
+    by bisection on their recomputed float64 scores.  Router selection must
+    match the oracle exactly."""
+    announce("subblock huge magnitudes: h=2 tiles=(1,70,1) sp=0.75, Q and K x 2^52")
+    h, s_t, n_v, s_a = 2, 64, 70, 64
+    s_v = n_v * T
+    x = synth.vsa_inputs(28, h, s_t, s_v, s_a)
+    for n in ("q", "k"):
+        x[n] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x[n]) * np.float32(2.0 ** 52))
+    xd = G.inputs_to_dev({n: x[n] for n in ("q", "k")})
+    kk = bsv.vsa_subblock_count(s_v, 0.75)
+    ws = torch.empty(bsv.vsa_subblock_workspace_bytes(h, s_t, s_v, s_a), dtype=torch.uint8,
+                     device="cuda")
+    sel = torch.full((h, n_v, kk), -7, dtype=torch.int32, device="cuda")
+    bsv.vsa_subblock_select(xd["q"], xd["k"], s_t, s_v, s_a, 0.75, sel, ws)
+    torch.cuda.synchronize()
+    ref = oracle.subblock_select(x["q"], x["k"], s_t, s_v, s_a, 0.75, want_scores=True,
+                                 threads=THREADS)
+    qs, ks = read_subs(ws, h, s_t, s_v, s_a)
+    assert np.linalg.norm(qs.astype(np.float64), axis=-1).max() ** 2 > 2.0 ** 100
+    check_rows(sel.cpu().numpy().reshape(-1, kk), ref["sel"].reshape(-1, kk),
+               ref["scores"].reshape(-1, n_v), ref["kth"].reshape(-1), exempt_ok=False)
+
+
 def test_zero_queries_take_lowest_indices():
     announce("subblock Q = 0: every score log 16")
     h, s_t, n_v, s_a = 2, 64, 40, 64
