@@ -208,18 +208,20 @@ def test_close_pairs_decided_in_float64(log2_w0):
         assert tied >= n_v, tied
 
 
-def test_huge_magnitudes_rank_every_key_in_float64():
-    """Q and K scaled by 2^52 (exact in bf16): |Qbar_u| max|Kbar_w| exceeds
-    2^100, where the float32 score products could leave their range, so
-    every row is ranked by recomputed float64 scores.  Selection must match
-    the oracle exactly (the coarse branch is not checked: its float32 score
-    rows cannot hold these magnitudes to the bar)."""
-    announce("huge magnitudes: h=2 tiles=(1,70,1) frac=0.2, Q and K x 2^52")
+@pytest.mark.parametrize("log2_scale", [40, 52])
+def test_huge_magnitudes_rank_every_key_in_float64(log2_scale):
+    """Q and K scaled by 2^40 or 2^52 (exact in bf16).  At 2^40 the float32
+    scores and their error bound decide as usual; at 2^52 |Qbar_u|
+    max|Kbar_w| exceeds 2^100, where the float32 score products could leave
+    their range, so every row is ranked by recomputed float64 scores.
+    Selection must match the oracle exactly (the coarse branch is not
+    checked: float32 score rows do not hold such magnitudes to its bar)."""
+    announce(f"huge magnitudes: h=2 tiles=(1,70,1) frac=0.2, Q and K x 2^{log2_scale}")
     h, s_t, n_v, s_a = 2, 64, 70, 64
     s_v = n_v * T
     x = synth.vsa_inputs(27, h, s_t, s_v, s_a)
     for n in ("q", "k"):
-        x[n] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x[n]) * np.float32(2.0 ** 52))
+        x[n] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x[n]) * np.float32(2.0 ** log2_scale))
     xd = G.inputs_to_dev(x)
     kk = bsv.vsa_topk_count(s_v, 0.2)
     ws = torch.empty(bsv.vsa_workspace_bytes(h, s_t, s_v, s_a, 0.2), dtype=torch.uint8, device="cuda")
@@ -231,7 +233,7 @@ def test_huge_magnitudes_rank_every_key_in_float64():
     w = G.read_workspace(ws, h, s_t, s_v, s_a)
     qn = np.linalg.norm(w["qbar64"], axis=-1).min()
     kn = np.linalg.norm(w["kbar"].astype(np.float64), axis=-1).max()
-    assert qn * kn > 2.0 ** 100, (qn, kn)
+    assert (qn * kn > 2.0 ** 100) == (log2_scale == 52), (qn, kn)
     G.check_selection(sel.cpu().numpy(), ref, exempt_ok=False)
 
 

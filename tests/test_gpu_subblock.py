@@ -205,17 +205,20 @@ def test_all_key_tiles_equal():
     assert np.array_equal(sel, np.broadcast_to(np.arange(ref["k"]), sel.shape))
 
 
-def test_huge_magnitudes_rank_every_key_in_float64():
-    """Q and K scaled by 2^52 (exact in bf16): the logit bounds exceed 2^100,
-    so every key of every row is in the band, more than 64 keys are ranked
-    by bisection on their recomputed float64 scores.  Router selection must
-    match the oracle exactly."""
-    announce("subblock huge magnitudes: h=2 tiles=(1,70,1) sp=0.75, Q and K x 2^52")
+@pytest.mark.parametrize("log2_scale", [46, 52])
+def test_huge_magnitudes_rank_every_key_in_float64(log2_scale):
+    """Q and K scaled by 2^46 or 2^52 (exact in bf16).  At 2^46 the logits
+    reach ~2^90 and the float32 scores and their bounds decide as usual (a
+    fused x - m in the log-sum-exp overflowed here); at 2^52 the bounds
+    exceed 2^100, so every key of every row is in the band and more than 64
+    keys are ranked by bisection on their recomputed float64 scores.  Router
+    selection must match the oracle exactly."""
+    announce(f"subblock huge magnitudes: h=2 tiles=(1,70,1) sp=0.75, Q and K x 2^{log2_scale}")
     h, s_t, n_v, s_a = 2, 64, 70, 64
     s_v = n_v * T
     x = synth.vsa_inputs(28, h, s_t, s_v, s_a)
     for n in ("q", "k"):
-        x[n] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x[n]) * np.float32(2.0 ** 52))
+        x[n] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(x[n]) * np.float32(2.0 ** log2_scale))
     xd = G.inputs_to_dev({n: x[n] for n in ("q", "k")})
     kk = bsv.vsa_subblock_count(s_v, 0.75)
     ws = torch.empty(bsv.vsa_subblock_workspace_bytes(h, s_t, s_v, s_a), dtype=torch.uint8,
@@ -226,7 +229,8 @@ def test_huge_magnitudes_rank_every_key_in_float64():
     ref = oracle.subblock_select(x["q"], x["k"], s_t, s_v, s_a, 0.75, want_scores=True,
                                  threads=THREADS)
     qs, ks = read_subs(ws, h, s_t, s_v, s_a)
-    assert np.linalg.norm(qs.astype(np.float64), axis=-1).max() ** 2 > 2.0 ** 100
+    n2 = np.linalg.norm(qs.astype(np.float64), axis=-1).max() ** 2
+    assert n2 > 2.0 ** 90 and (n2 > 2.0 ** 100) == (log2_scale == 52), np.log2(n2)
     check_rows(sel.cpu().numpy().reshape(-1, kk), ref["sel"].reshape(-1, kk),
                ref["scores"].reshape(-1, n_v), ref["kth"].reshape(-1), exempt_ok=False)
 
