@@ -49,7 +49,10 @@ __device__ __forceinline__ uint64_t uniform_key(uint64_t x) {
 
 // The kk-th largest of the keys a wavefront holds (kk >= 1, at least kk keys
 // nonzero; zero keys are absent), by bisection on the key value; `gt`
-// returns the number of keys above it.
+// returns the number of keys above it.  The search stops at the first probe
+// that exactly kk keys reach (about log2 of the row length probes for
+// spread-out keys instead of one per key bit); the kk-th largest key is then
+// the smallest key at or above that probe.
 template <typename Key, int NS>
 __device__ __forceinline__ Key kth_largest(const Key (&kv)[NS], uint32_t kk, uint32_t& gt) {
     Key kmin = ~(Key)0, kmax = 0;
@@ -74,19 +77,33 @@ __device__ __forceinline__ Key kth_largest(const Key (&kv)[NS], uint32_t kk, uin
         for (int i = 0; i < NS; ++i) c += (uint32_t)__popcll(__ballot(kv[i] >= th));
         return c;
     };
-    // the answer is the largest T with count_ge(T) >= kk, a key value in
-    // [kmin, kmax]; invariant: count_ge(lo) >= kk and the answer is <= hi
+    // invariant: count_ge(lo) >= kk, and the answer (the largest T with
+    // count_ge(T) >= kk, a key value) is in [lo, hi]
     Key lo = kmin, hi = kmax;
     while (lo < hi) {
         const Key mid = lo + (Key)((hi - lo + 1) >> 1);
-        if (count_ge(mid) >= kk) lo = mid;
-        else hi = mid - 1;
+        const uint32_t c = count_ge(mid);
+        if (c >= kk) {
+            lo = mid;
+            if (c == kk) break;  // the keys >= mid are exactly the kk largest
+        } else {
+            hi = mid - 1;
+        }
     }
+    Key t = ~(Key)0;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) t = (kv[i] >= lo && kv[i] < t) ? kv[i] : t;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const Key a = __shfl_xor(t, off);
+        t = a < t ? a : t;
+    }
+    t = uniform_key(t);
     uint32_t c = 0;
 #pragma unroll
-    for (int i = 0; i < NS; ++i) c += (uint32_t)__popcll(__ballot(kv[i] > lo));
+    for (int i = 0; i < NS; ++i) c += (uint32_t)__popcll(__ballot(kv[i] > t));
     gt = c;
-    return lo;
+    return t;
 }
 
 // Exact k-th largest of one row's keys by bisection on the 64-bit key value,
