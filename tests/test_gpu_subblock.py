@@ -265,11 +265,13 @@ def test_deterministic_and_library_workspace():
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("n_v", [1300, 2700])
+@pytest.mark.parametrize("n_v", [1280, 1300, 2700])
 def test_long_rows(n_v):
-    """Rows longer than 1,280 tiles take the 8-row (n_v <= 2,560) and 4-row
-    workgroups with longer register rows in the top-k; every selection row is
-    checked, outputs on sampled rows."""
+    """n_v = 1,280 fills the two-workgroups-per-CU router (8 rows of 1,280
+    slots, 80 KiB of LDS each, 20 keys per lane in the top-k); longer rows
+    take the 8-row (n_v <= 2,560) and 4-row workgroups, one per CU, with
+    longer register rows in the top-k.  Every selection row is checked,
+    outputs on sampled rows."""
     h, s_t, s_a = 1, 64, 64
     s_v = n_v * T
     sp = 0.8
