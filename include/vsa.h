@@ -23,6 +23,10 @@
  *     the tile's 64 rows;
  *   - out = O_fine + sigmoid(G) * O_coarse on video rows, out = O_fine on
  *     text and audio rows; softmax scale 1/sqrt(128); fp32 accumulation.
+ * The device forms the tile scores on the float32 matrix unit with a proven
+ * bound on their error and recomputes the float64 score wherever that bound
+ * leaves the ranking open, so the selection is exactly that of the float64
+ * scores above; the coarse softmax uses the float32 scores.
  *
  * Layout.  q, k, v, gate and out are bfloat16, token-major [S][H][128]
  * (element (s,h,d) at index (s*H + h)*128 + d), S = text_len + video_len +
@@ -204,7 +208,10 @@ vsa_status vsa_forward_padded(const void* q, const void* k, const void* v, const
  *   score(u, w) = log sum over the 16 pairs (a, b) of exp(x_ab),
  * which estimates the unnormalised softmax mass of key tile w for query tile
  * u.  The kept count is vsa_subblock_count(video_len, sparsity); ties in the
- * ranking go to the lower tile index.  Text and audio queries attend to every
+ * ranking go to the lower tile index.  As for the tile scores, the device
+ * computes in float32 with error bounds and recomputes in float64 where the
+ * bounds leave the ranking open (float64 exp and log, so scores tied to
+ * within their rounding may order differently from a host evaluation).  Text and audio queries attend to every
  * key, video queries to every text and audio key and to their kept video
  * tiles; there is no coarse branch and no gate (out = O_fine).
  *
