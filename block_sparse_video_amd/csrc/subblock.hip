@@ -413,10 +413,8 @@ __device__ void select_row_band(uint64_t* row, int n_v, int k, bool zero_q, int 
 // that XCD's L2 while its CUs share them.
 template <int RT, int NS, int MINB>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2 * MINB))) void
-subblock_route_kernel(const float* __restrict__ qsub,
-                                                             const float* __restrict__ ksub,
-                                                             int H, int n_v, int n_c, int k,
-                                                             int ldw, int32_t* __restrict__ sel) {
+subblock_route_kernel(const float* __restrict__ qsub, const float* __restrict__ ksub, int H,
+                      int n_v, int n_c, int k, int ldw, int32_t* __restrict__ sel) {
     extern __shared__ __align__(16) unsigned char smem[];
     uint64_t* sc = (uint64_t*)smem;  // [4 RT][ldw] score slots
     constexpr int PH = 8 / RT;
@@ -463,7 +461,7 @@ subblock_route_kernel(const float* __restrict__ qsub,
         };
         // key groups: the packed means of tiles past n_v are zero (subpool)
         auto issue_keys = [&](int c, float (&bq)[32]) {
-            const float4* p = (const float4*)(kh + (int64_t)c * 2048) + ((lane & 48) | (lane & 15));
+            const float4* p = (const float4*)(kh + (int64_t)c * 2048) + lane;  // row lane % 16, dims 32 (lane / 16) + ...
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float4 t = p[64 * i];
