@@ -22,7 +22,8 @@
 // 128 bytes per instruction; each wavefront copies 32 rows of W and 32 of X
 // per stage) one stage ahead; one barrier per stage both publishes the next
 // stage and frees the current buffer for the stage after it; operands are
-// read from LDS one MFMA step ahead of their use.
+// read from LDS one MFMA step ahead of their use, the reads spread between
+// the MFMAs.
 #include "vsa_internal.h"
 
 namespace vsa {
@@ -164,6 +165,18 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) xb[j] = *(lds_bf16x8_ptr)(uintptr_t)(st + ox[s2][j]);
     };
+    // the next step's six operand reads, issued in source order before this
+    // step's eight MFMAs, are spread one after each of the first six MFMAs
+    // (issued as a burst they queue in the LDS behind the other waves' reads
+    // and copies: 19.7 against 18.8 ms on the 10 s projections)
+    auto interleave = [&]() {
+#pragma unroll
+        for (int g = 0; g < 6; ++g) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    };
     auto mfma_step = [&](const bf16x8 (&wa)[4], const bf16x8 (&xb)[2]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -186,10 +199,13 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
         const int buf = kt & 1;
         read_ops(wa1, xb1, buf, 1);
         mfma_step(wa0, xb0);
+        interleave();
         read_ops(wa0, xb0, buf, 2);
         mfma_step(wa1, xb1);
+        interleave();
         read_ops(wa1, xb1, buf, 3);
         mfma_step(wa0, xb0);
+        interleave();
         if (kt + 1 < KT) {
             wait_vm(0);
             barrier();
