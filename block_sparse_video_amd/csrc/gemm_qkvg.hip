@@ -168,7 +168,7 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
     // the next step's six operand reads, issued in source order before this
     // step's eight MFMAs, are spread one after each of the first six MFMAs
     // (issued as a burst they queue in the LDS behind the other waves' reads
-    // and copies: 19.7 against 18.8 ms on the 10 s projections)
+    // and copies: 19.7 against 18.7 ms on the 10 s projections)
     auto interleave = [&]() {
 #pragma unroll
         for (int g = 0; g < 6; ++g) {
@@ -210,9 +210,13 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
             wait_vm(0);
             barrier();
             if (kt + 2 < KT) fetch_stage(buf, (kt + 2) * kBK);
-            read_ops(wa0, xb0, buf ^ 1, 0);
         }
+        // issued in every stage so that the reads interleave with this step's
+        // MFMAs; after the last stage they read the other buffer's stale
+        // values, which are never used
+        read_ops(wa0, xb0, buf ^ 1, 0);
         mfma_step(wa1, xb1);
+        interleave();
     }
     barrier();  // every wave is done with the ring before it becomes staging
 
