@@ -126,6 +126,14 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
         }
     }
     // 4 W and 4 X copies of 1 KiB (8 rows of 128 bytes each) for stage buffer `buf`
+    auto fetch_w = [&](int buf, int k0) {
+        const uint32_t st = lds0 + (uint32_t)buf * kStageBytes;
+        fetch4(st + 4096u * wave, wbase + k0, wo);  // W rows 32 wave .. +31
+    };
+    auto fetch_x = [&](int buf, int k0) {
+        const uint32_t st = lds0 + (uint32_t)buf * kStageBytes;
+        fetch4(st + 32768u + 4096u * wave, xbase + k0, xo);  // X rows 32 wave .. +31
+    };
     auto fetch_stage = [&](int buf, int k0) {
         const uint32_t st = lds0 + (uint32_t)buf * kStageBytes;
         fetch4(st + 4096u * wave, wbase + k0, wo);           // W rows 32 wave .. +31
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
     // the next step's six operand reads, issued in source order before this
     // step's eight MFMAs, are spread one after each of the first six MFMAs
     // (issued as a burst they queue in the LDS behind the other waves' reads
-    // and copies: 19.7 against 18.7 ms on the 10 s projections)
+    // and copies)
     auto interleave = [&]() {
 #pragma unroll
         for (int g = 0; g < 6; ++g) {
@@ -209,7 +217,7 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
         if (kt + 1 < KT) {
             wait_vm(0);
             barrier();
-            if (kt + 2 < KT) fetch_stage(buf, (kt + 2) * kBK);
+            if (kt + 2 < KT) fetch_w(buf, (kt + 2) * kBK);
         }
         // issued in every stage so that the reads interleave with this step's
         // MFMAs; after the last stage they read the other buffer's stale
@@ -217,6 +225,9 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
         read_ops(wa0, xb0, buf ^ 1, 0);
         mfma_step(wa1, xb1);
         interleave();
+        // the X half of stage kt + 2 one step after its W half, so that the
+        // copies do not all land in the LDS at once
+        if (kt + 2 < KT) fetch_x(buf, (kt + 2) * kBK);
     }
     barrier();  // every wave is done with the ring before it becomes staging
 
