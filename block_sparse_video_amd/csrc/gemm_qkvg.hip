@@ -48,7 +48,8 @@ struct GemmArgs {
     uint16_t* out[4];    // [tokens][out] each
     int64_t tokens;
     int hidden, n_out;   // n_out = heads * 128, a multiple of 256
-    int tiles_n;         // n_out / 256 * 4
+    int tiles_n;         // n_out / 256 (the channel tiles of one projection)
+    int proj;            // the projection this launch computes (0 q, 1 k, 2 v, 3 gate)
 };
 
 __device__ __forceinline__ void wait_vm(int n) {
@@ -102,8 +103,8 @@ __global__ __launch_bounds__(512) void gemm_qkvg_kernel(GemmArgs a) {
     const int tn = in_band / band_t;
     const int tt = band * kBand + (in_band - tn * band_t);
 
-    const int proj = tn / (a.n_out / kBM);                 // 0..3
-    const int n0 = (tn - proj * (a.n_out / kBM)) * kBM;    // first channel
+    const int proj = a.proj;
+    const int n0 = tn * kBM;  // first channel
     const int64_t t0 = (int64_t)tt * kBT;                  // first token
     const int K = a.hidden;
     const uint16_t* wbase = a.w + ((int64_t)proj * a.n_out + n0) * K;
@@ -277,10 +278,19 @@ hipError_t launch_project_qkvg(const uint16_t* x, const uint16_t* w, uint16_t* c
     a.tokens = tokens;
     a.hidden = hidden;
     a.n_out = n_out;
-    a.tiles_n = 4 * (n_out / kBM);
+    a.tiles_n = n_out / kBM;
     const int64_t tiles = ((tokens + kBT - 1) / kBT) * a.tiles_n;
-    hipLaunchKernelGGL(gemm_qkvg_kernel, dim3((unsigned)tiles), dim3(512), kStages * kStageBytes, stream, a);
-    return hipGetLastError();
+    // one launch per projection: its 77 MB of weights (10 s shape) stay in
+    // the 256 MB last-level cache while every token band streams past them,
+    // where the four projections' 308 MB together did not fit
+    for (int p = 0; p < 4; ++p) {
+        a.proj = p;
+        hipLaunchKernelGGL(gemm_qkvg_kernel, dim3((unsigned)tiles), dim3(512),
+                           kStages * kStageBytes, stream, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace vsa
