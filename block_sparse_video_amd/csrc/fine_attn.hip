@@ -68,7 +68,7 @@ struct FineArgs {
     const int32_t* sel;
     const float* coarse;
     uint16_t* out;
-    uint32_t* sched;    // kQueues + 2 work-queue counters, 32 words apart, zero at launch
+    uint32_t* sched;    // kQueues + 4 work-queue counters, 32 words apart, zero at launch
     float* partial;     // dense parts: [dense unit][part][64 x 128 O, 64 l, 64 reference]
     int parts;          // key-list parts per dense unit (1: no split)
     int check_sel;      // nonzero: validate each selection row before use (caller-supplied rows)
@@ -80,17 +80,18 @@ struct FineArgs {
 // Work queues.  The kernel is persistent: one workgroup per wavefront slot,
 // each taking units (head h, query tile j) from shared counters until every
 // queue is empty.  Two kinds of queue:
-//  - video queues, one per head group: with an even head count, XCDs 0-3
-//    take the even heads' video units and XCDs 4-7 the odd heads', from one
-//    counter per group, in head-major order, query tiles ascending.  Two
-//    heads are then in flight at a time, each pulled into four L2s instead
-//    of eight while both stay within the last-level cache, and the four
-//    XCDs of a group always work on the same head: an XCD that runs slower
-//    simply takes fewer units.  (With one queue per XCD the XCDs of a group
-//    drift apart on inputs whose selections cluster around each query tile:
-//    a lagging XCD's units slow down further and the group ends up spread
-//    over several heads.)  With an odd head count all video units are in
-//    one queue for all eight XCDs;
+//  - video queues, one per head group: with NG groups (4 when the head count
+//    is a multiple of 4, 2 when it is even, else 1), XCDs 8G/NG .. take the
+//    video units of heads h = G mod NG from one counter per group, in
+//    head-major order, query tiles ascending.  NG heads are then in flight at
+//    a time, each pulled into 8/NG L2s, all of them within the last-level
+//    cache, and the XCDs of a group always work on the same head: an XCD that
+//    runs slower simply takes fewer units.  (With one queue per XCD the XCDs
+//    of a group drift apart on inputs whose selections cluster around each
+//    query tile: a lagging XCD's units slow down further and the group ends
+//    up spread over several heads.  On such inputs two XCDs per head also
+//    keep neighbouring query tiles, which share key tiles, in fewer L2s than
+//    four do.);
 //  - dense queues, one per XCD: a contiguous 1/8 share of the dense
 //    (text/audio query) items, ordered by head, then key-list part, then
 //    query tile.  A dense unit's list is every tile (~4.5x a video unit's),
@@ -100,15 +101,17 @@ struct FineArgs {
 //    first measured 15-20% slower: the video units then start unevenly).
 // Counters: dense queue x at word 32x, video queue G at word 32 (8 + G).
 constexpr int kVideoQueue = kQueues;  // queue index of head group 0's video queue
+constexpr int kVideoQueues = 4;       // at most four head groups
+
+__device__ __forceinline__ int video_groups(int H) { return (H & 3) == 0 ? 4 : ((H & 1) == 0 ? 2 : 1); }
 
 __device__ __forceinline__ int dense_begin(int D, int x) { return (int)(((int64_t)D * x) / kQueues); }
 
 // Units in queue q (dense: q < 8; video: q = kVideoQueue + G).
 __device__ __forceinline__ int queue_count(int H, int n_v, int D, int q) {
     if (q < kQueues) return dense_begin(D, q + 1) - dense_begin(D, q);
-    const int G = q - kVideoQueue;
-    if ((H & 1) == 0) return (H >> 1) * n_v;
-    return G == 0 ? H * n_v : 0;
+    const int G = q - kVideoQueue, NG = video_groups(H);
+    return G < NG ? (H / NG) * n_v : 0;
 }
 
 // Unit i of queue q -> (h, j) and, for a dense unit, its key-list part p.
@@ -125,21 +128,21 @@ __device__ __forceinline__ void queue_unit(int H, int n_t, int n_v, int n_a, int
         j = t < n_t ? t : n_v + t;
     } else {
         const int hh = i / n_v;
-        h = (H & 1) == 0 ? 2 * hh + (q - kVideoQueue) : hh;
+        h = video_groups(H) * hh + (q - kVideoQueue);
         j = n_t + (i - hh * n_v);
     }
 }
 
 // Queue s of the order a workgroup on XCD xcc tries: its group's video
-// queue (the only one with an odd head count), its own dense queue, the other dense queues of its group, then the
-// other group's video queue and the remaining dense queues, so that faster
-// XCDs take units from slower ones and no slot idles while work remains.
+// queue, its own dense queue, the other XCDs' dense queues, then the other
+// groups' video queues (empty ones are skipped), so that faster XCDs take
+// units from slower ones and no slot idles while work remains.
 __device__ __forceinline__ int queue_order(int H, int xcc, int s) {
-    const int G = (H & 1) ? 0 : (xcc >> 2);  // one video queue for all XCDs with odd H
+    const int NG = video_groups(H);
+    const int G = xcc / (kQueues / NG);
     if (s == 0) return kVideoQueue + G;
-    if (s <= 4) return (xcc & 4) | ((xcc + s - 1) & 3);
-    if (s == 5) return kVideoQueue + (G ^ 1);
-    return (~xcc & 4) | ((xcc + s - 6) & 3);
+    if (s <= kQueues) return (xcc + s - 1) & (kQueues - 1);
+    return kVideoQueue + (G + s - kQueues) % NG;
 }
 
 // Returns the index of the next unit in queue `q`, or -1 when every queue is
@@ -148,7 +151,7 @@ __device__ __forceinline__ int next_unit(uint32_t* sched, int H, int n_t, int n_
                                          int xcc, uint32_t& empty, int& q) {
     const int D = H * P * (n_t + n_a);
 #pragma unroll 1
-    for (int s = 0; s < kQueues + 2; ++s) {
+    for (int s = 0; s < kQueues + kVideoQueues; ++s) {
         q = queue_order(H, xcc, s);
         if ((empty >> q) & 1u) continue;
         const int count = queue_count(H, n_v, D, q);
@@ -164,7 +167,7 @@ __device__ __forceinline__ int next_unit(uint32_t* sched, int H, int n_t, int n_
 }
 
 __global__ void clear_sched_kernel(uint32_t* sched) {
-    for (int i = threadIdx.x; i < 32 * (kQueues + 2); i += blockDim.x) sched[i] = 0u;
+    for (int i = threadIdx.x; i < 32 * (kQueues + kVideoQueues); i += blockDim.x) sched[i] = 0u;
 }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {

@@ -54,7 +54,7 @@ struct Layout {
     size_t kpack;   // bf16   [H][N][2][8][64][8]      K tiles in MFMA A-operand order
     size_t vpack;   // bf16   [H][N][2][4][2][64][8]   V^T tiles in MFMA A-operand order
     size_t partial; // float  [H][n_t+n_a][parts][64*128 + 128]  split dense units' partial results
-    size_t sched;   // uint32 [10][32] fine-attention work-queue counters (one 128-byte line each)
+    size_t sched;   // uint32 [12][32] fine-attention work-queue counters (one 128-byte line each)
     size_t qsub;    // float  [H][n_c][8][64][4]  SubBlock router: Q sub-block means (0 bytes
     size_t ksub;    // float  [H][n_c][8][64][4]  without the router), n_c = ceil(n_v / 4)
     size_t total;
@@ -67,10 +67,10 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 constexpr int kSubblockMaxTiles = 5120;
 
 // Fine-attention work queues: kQueues dense (text/audio unit) queues, one per
-// XCD, then one video-unit queue per head group of four XCDs; each counter on
-// its own 128-byte line.
+// XCD, then up to four video-unit queues, one per head group of XCDs; each
+// counter on its own 128-byte line.
 constexpr int kQueues = 8;
-constexpr size_t kSchedBytes = (kQueues + 2) * 128;
+constexpr size_t kSchedBytes = (kQueues + 4) * 128;
 // A dense (text/audio query) unit's key list is split into at most this many
 // parts; one part's record is 64 x 128 unnormalised outputs, 64 denominators
 // and 64 softmax references, float32.

@@ -113,8 +113,8 @@ size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_le
  *              the total lie the partial results of text/audio query tiles
  *              whose key list the fine stage splits into parts (float32,
  *              33,280 bytes per part, up to 4 parts per tile; none without
- *              video tiles) and, in the last 1,280 bytes, the fine
- *              stage's ten work-queue counters, which every call clears
+ *              video tiles) and, in the last 1,536 bytes, the fine
+ *              stage's twelve work-queue counters, which every call clears
  *              before use
  * Returns VSA_OK or a shape error.  Host only. */
 vsa_status vsa_workspace_layout(int32_t num_heads, int64_t text_len, int64_t video_len,

@@ -297,11 +297,11 @@ def test_subblock_whole_validation():
 
 
 def test_subblock_whole_workspace_and_count():
-    # kpack + vpack of every tile, the 1,280 bytes of queue counters (ten 128-byte
-    # lines), then the two piece-mean regions
+    # kpack + vpack of every tile, the 1,536 bytes of queue counters (twelve
+    # 128-byte lines), then the two piece-mean regions
     h, n = 56, 1166
     n_c = (n + 3) // 4
     total = bsv.vsa_subblock_whole_workspace_bytes(h, 1024, 72576, 1024)
-    assert total == 2 * h * n * 16384 + 1280 + 2 * h * n_c * 8192
+    assert total == 2 * h * n * 16384 + 1536 + 2 * h * n_c * 8192
     assert bsv.vsa_subblock_count(74624, 0.75) == 288   # the whole-sequence kept count
     assert bsv.vsa_subblock_whole_workspace_bytes(1, 64, 64 * 5119, 64) == 0
