@@ -795,16 +795,6 @@ __global__ __launch_bounds__(256) void combine_parts_kernel(FineArgs a) {
 
 }  // namespace
 
-// Key-list parts of a dense unit: about the length of a video unit's list
-// (so that no unit is much longer than the rest), at most kMaxParts; 1
-// without video tiles.
-int dense_parts(const Shape& s) {
-    if (s.n_v == 0 || s.n_t + s.n_a == 0) return 1;
-    const int lv = s.n_t + s.k + s.n_a;
-    int p = (int)((double)s.N / (double)lv + 0.5);
-    return p < 1 ? 1 : (p > kMaxParts ? kMaxParts : p);
-}
-
 // Wavefront slots of the device: 4 per CU (40 KiB of LDS each), cached per device.
 int fine_slots() {
     static std::atomic<int> slots[kMaxDevices];

@@ -53,7 +53,7 @@ struct Layout {
     size_t coarse;  // float  [H][n_v][128]
     size_t kpack;   // bf16   [H][N][2][8][64][8]      K tiles in MFMA A-operand order
     size_t vpack;   // bf16   [H][N][2][4][2][64][8]   V^T tiles in MFMA A-operand order
-    size_t partial; // float  [H][n_t+n_a][parts][64*128 + 128]  split dense units' partial results
+    size_t partial; // float  [H][n_t+n_a][kMaxParts][64*128 + 128]  split dense units' partial results
     size_t sched;   // uint32 [12][32] fine-attention work-queue counters (one 128-byte line each)
     size_t qsub;    // float  [H][n_c][8][64][4]  SubBlock router: Q sub-block means (0 bytes
     size_t ksub;    // float  [H][n_c][8][64][4]  without the router), n_c = ceil(n_v / 4)
@@ -74,8 +74,21 @@ constexpr size_t kSchedBytes = (kQueues + 4) * 128;
 // A dense (text/audio query) unit's key list is split into at most this many
 // parts; one part's record is 64 x 128 unnormalised outputs, 64 denominators
 // and 64 softmax references, float32.
-constexpr int kMaxParts = 4;
+constexpr int kMaxParts = 8;
 constexpr size_t kPartBytes = (64 * 128 + 128) * sizeof(float);
+
+// Key-list parts of a dense unit: about half the length of a video unit's
+// list, at most kMaxParts; 1 without video tiles.  No unit is then much
+// longer than the rest, and the dense parts that close the queues are short,
+// so the launch ends with little idle time.  The count depends on the
+// per-head shape only, so a call split into groups of heads splits its
+// dense units exactly as the whole call does.
+inline int dense_parts(const Shape& s) {
+    if (s.n_v == 0 || s.n_t + s.n_a == 0) return 1;
+    const int lv = s.n_t + s.k + s.n_a;
+    int p = (int)(2.0 * (double)s.N / (double)lv + 0.5);
+    return p < 1 ? 1 : (p > kMaxParts ? kMaxParts : p);
+}
 
 // Storage order of the 128 dims of a pooled Q or K row: dim d = 4 s + g sits
 // at position 32 g + s, so that the score MFMAs' lane group g (which feeds
@@ -100,6 +113,8 @@ inline Layout make_layout(const Shape& s, bool subblock = false, bool pooled = t
     L.vpack = off;  off = align_up(off + (size_t)s.H * (size_t)s.N * kT * kD * 2);
     const size_t sub = subblock ? (size_t)s.H * (size_t)((s.n_v + 3) / 4) * 2048 * sizeof(float) : 0;
     const size_t dense_units = (size_t)s.H * (size_t)(s.n_t + s.n_a);
+    // sized for kMaxParts, so that the layout does not depend on k (which the
+    // layout query does not take)
     L.partial = off; off = align_up(off + (s.n_v > 0 ? dense_units * kMaxParts * kPartBytes : 0));
     L.sched = off;  off = align_up(off + kSchedBytes);
     L.qsub = off;   off = align_up(off + sub);

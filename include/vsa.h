@@ -112,7 +112,7 @@ size_t vsa_workspace_bytes(int32_t num_heads, int64_t text_len, int64_t video_le
  *   offsets[6] total bytes (= vsa_workspace_bytes).  Between packed V and
  *              the total lie the partial results of text/audio query tiles
  *              whose key list the fine stage splits into parts (float32,
- *              33,280 bytes per part, up to 4 parts per tile; none without
+ *              33,280 bytes per part, up to 8 parts per tile; none without
  *              video tiles) and, in the last 1,536 bytes, the fine
  *              stage's twelve work-queue counters, which every call clears
  *              before use

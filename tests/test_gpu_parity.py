@@ -346,11 +346,12 @@ def test_late_large_scores_recompute():
 
 def test_split_dense_units_combine_parts():
     """A text/audio query tile's key list is walked as several parts (here
-    3: N = 24 tiles, video lists of 8) whose outputs are merged with weights
-    2^(m_p - max m).  Scores grow by ~0.5 (log2 units) per key tile, so the
-    three parts start from references about 4 apart and all contribute; a
-    merge that ignored the references would be far off.  Video query tiles
-    select the last k video tiles (pooled scores grow with the tile index)."""
+    6: N = 24 tiles, video lists of 8, parts of about half a list) whose
+    outputs are merged with weights 2^(m_p - max m).  Scores grow by ~0.5
+    (log2 units) per key tile, so the parts start from references about 2
+    apart and all contribute; a merge that ignored the references would be
+    far off.  Video query tiles select the last k video tiles (pooled scores
+    grow with the tile index)."""
     announce("split dense units: h=1 tiles=(2,20,2)")
     h, s_t, n_v, s_a = 1, 128, 20, 128
     s_v = n_v * T
