@@ -36,8 +36,8 @@ def _both(x, s_t, s_v, s_a, frac):
 
 
 def test_noalloc_matches_forward_twice_second_smaller():
-    # first call: 14 heads at the 5 s shape, ~24 MB of workspace per head, so
-    # the 256 MiB array takes the heads in two groups (11 + 3)
+    # first call: 14 heads at the 5 s shape, ~27 MB of workspace per head, so
+    # the 256 MiB array takes the heads in two groups (9 + 5)
     h, s_t, s_v, s_a = 14, 1024, 36288, 512
     print(f"[case] noalloc 1: h={h} ({s_t},{s_v},{s_a})", flush=True)
     x = synth.vsa_inputs(0, h, s_t, s_v, s_a, threads=THREADS)
