@@ -95,9 +95,9 @@ struct FineArgs {
 //  - dense queues, one per XCD: a contiguous 1/8 share of the dense
 //    (text/audio query) items, ordered by head, then key-list part, then
 //    query tile.  A dense unit's list is every tile (~4.5x a video unit's),
-//    so it is walked as P parts of about a video unit's length and the parts
-//    are combined afterwards; the parts of one head share one L2 and sweep
-//    their key ranges in step.  They follow the video units (dense items
+//    so it is walked as P parts of about half a video unit's length and the
+//    parts are combined afterwards; the parts of one head share one L2 and
+//    sweep their key ranges in step.  They follow the video units (dense items
 //    first measured 15-20% slower: the video units then start unevenly).
 // Counters: dense queue x at word 32x, video queue G at word 32 (8 + G).
 constexpr int kVideoQueue = kQueues;  // queue index of head group 0's video queue
