@@ -477,6 +477,9 @@ BIG = {
     "5s_14h": (14, 1024, 36288, 512),
     "10s_14h": (14, 1024, 72576, 1024),
     "10s_56h": (56, 1024, 72576, 1024),
+    # an odd head count: one video queue shared by all eight XCDs (14 heads
+    # give two head groups, 56 give four)
+    "10s_7h": (7, 1024, 72576, 1024),
 }
 
 
